@@ -1,0 +1,283 @@
+"""Synthetic rollout traces, compaction-event records and paged block tables.
+
+The rules below stand in for the rollouts of the KV-streams paper
+("KV-streams for Efficient Compaction in Agentic Reinforcement Learning",
+Penaloza et al.).  The pages fix only the qualitative structure:
+
+* a rollout is a prompt followed by turns; when the live context reaches its
+  budget a compaction event removes older turns and keeps the prompt, recent
+  turns or a summary (wqu.guru explainer, opening paragraphs; paper page,
+  Fig. 2B "P: prompt; S: summary");
+* whole turns are removed, boundary tokens included (explainer, paragraph on
+  token-level eviction);
+* every completion is padded to a multiple of 16 tokens so that events fall on
+  16-token block boundaries (explainer, paragraph on vLLM's 16-token blocks);
+* the trainer replays the recorded events as a mask over one continuous trace
+  (explainer, paragraph on the trainer; paper page, Fig. 2A).
+
+Everything quantitative (turn-length law, trigger, how much is evicted) is a
+reading stated in the docstrings here.  This module only *constructs inputs*:
+it never computes attention, RoPE or a compacted table.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+KS_NEVER = 2**31 - 1      # e_j of a token that is never evicted
+BLOCK = 16                # tokens per KV block
+
+
+def _round_up16(x: int) -> int:
+    return (int(x) + 15) // 16 * 16
+
+
+@dataclass
+class Trace:
+    """One continuous rollout trace and its compaction history.
+
+    ``e[j]`` is the trace index of the event that evicted token ``j``
+    (``KS_NEVER`` if never evicted); query ``i`` may attend key ``j`` iff
+    ``j <= i < e[j]``.  An event at index ``t`` fires after token ``t-1`` and
+    before token ``t`` is generated, so token ``t-1`` still saw everything it
+    evicts.
+    """
+    N: int
+    P: int
+    budget: int
+    strategy: str
+    turns: list                      # [(start, end)] of non-prompt turns
+    events: list                     # sorted event indices
+    evicted: dict                    # event index -> [(a, b)] evicted spans
+    e: np.ndarray = field(repr=False)  # int32 [N]
+
+
+def build_trace(rng: np.random.Generator, N: int, P: int, budget: int,
+                strategy: str, turn_len=(64, 512), overlap: int = 0,
+                summary: int = 0) -> Trace:
+    """Build one trace.
+
+    Turn lengths are integers uniform on ``turn_len`` (inclusive), rounded up
+    to a multiple of 16; a fixed length is given as ``turn_len=(L, L)``.  The
+    last turn is cut at ``N``.
+
+    Trigger: at the end of a turn, if the live size plus the next turn's
+    length would exceed ``budget``, an event fires at that turn end.
+
+    Strategies:
+      ``recent``  pop the oldest complete non-prompt turns until live <= B/2
+                  (the prompt is pinned);
+      ``window``  the same, but the prompt is the oldest turn and may be popped;
+      ``summary`` keep the prompt and the last ``overlap + summary`` tokens
+                  before the event; everything else that is live is evicted.
+    """
+    if strategy not in ("recent", "window", "summary"):
+        raise ValueError(strategy)
+    lo, hi = turn_len
+    turns = []
+    t = P
+    while t < N:
+        L = _round_up16(rng.integers(lo, hi + 1)) if lo != hi else lo
+        end = min(t + L, N)
+        turns.append((t, end))
+        t = end
+
+    e = np.full(N, KS_NEVER, dtype=np.int64)
+    units = [(0, P)] if P > 0 else []   # live spans, oldest first
+    events, evicted = [], {}
+    for idx, (a, b) in enumerate(turns):
+        units.append((a, b))
+        if idx + 1 == len(turns):
+            break
+        nxt = turns[idx + 1][1] - turns[idx + 1][0]
+        live = sum(y - x for x, y in units)
+        if live + nxt <= budget:
+            continue
+        t_ev = b
+        out = []
+        if strategy in ("recent", "window"):
+            first = 0 if (strategy == "window" or P == 0) else 1
+            target = budget // 2
+            while live > target and len(units) > first + 1:
+                u = units.pop(first)
+                out.append(u)
+                live -= u[1] - u[0]
+        else:
+            keep_lo = t_ev - (overlap + summary)
+            kept = [units[0]] if P > 0 else []
+            for (x, y) in (units[1:] if P > 0 else units):
+                if y <= keep_lo:
+                    out.append((x, y))
+                elif x >= keep_lo:
+                    kept.append((x, y))
+                else:
+                    out.append((x, keep_lo))
+                    kept.append((keep_lo, y))
+            units = kept
+        for (x, y) in out:
+            e[x:y] = t_ev
+        events.append(t_ev)
+        evicted[t_ev] = out
+    return Trace(N=N, P=P, budget=budget, strategy=strategy, turns=turns,
+                 events=events, evicted=evicted, e=e.astype(np.int32))
+
+
+def check_trace(tr: Trace) -> None:
+    """Assert the structural invariants every generated trace must satisfy."""
+    N, e = tr.N, tr.e.astype(np.int64)
+    j = np.arange(N)
+    assert np.all(e > j), "e_j > j violated"
+    ev = set(tr.events)
+    assert all(int(x) in ev or int(x) == KS_NEVER for x in np.unique(e))
+    assert all(t % BLOCK == 0 for t in tr.events), "events must be 16-aligned"
+    assert all(x % BLOCK == 0 and (y % BLOCK == 0 or y == tr.N)
+               for (x, y) in tr.turns)
+    # live size at every query index is within budget:
+    # |live(i)| = (i+1) - #{j <= i : e_j <= i}
+    ev_hist = np.zeros(N + 1, dtype=np.int64)
+    fin = e[e < N]
+    np.add.at(ev_hist, fin, 1)
+    gone = np.cumsum(ev_hist)[:N]
+    live = (j + 1) - gone
+    assert live.max() <= tr.budget, (live.max(), tr.budget)
+    if tr.strategy in ("recent", "window"):
+        for (x, y) in tr.turns:
+            assert np.all(e[x:y] == e[x]), "window strategies evict whole turns"
+    if tr.strategy != "window" and tr.P > 0:
+        assert np.all(e[:tr.P] == KS_NEVER), "prompt pinned"
+
+
+def trace_blocks_keep(tr: Trace) -> np.ndarray:
+    """Keep flag per 16-token block of the trace after its last event.
+
+    A block is kept iff none of its tokens was evicted.  (Derived from the
+    per-token record; the oracle derives its expected table from the event
+    list instead.)
+    """
+    nb = (tr.N + BLOCK - 1) // BLOCK
+    pad = np.full(nb * BLOCK, KS_NEVER, dtype=np.int64)
+    pad[:tr.N] = tr.e
+    return (pad.reshape(nb, BLOCK) == KS_NEVER).all(axis=1).astype(np.uint8)
+
+
+@dataclass
+class DecodeBatch:
+    """Paged caches of several sequences before a run of compaction rounds.
+
+    ``table0``      int32 [B, MB] physical block ids before any round (-1 pad);
+                    logical block x of sequence b holds tokens [16x, 16x+16),
+                    and the last listed block is a fresh block that receives the
+                    decoded token.
+    ``nblk0``       int32 [B] listed blocks before any round.
+    ``keeps``       uint8 [R, B, MB] keep flags for round r, relative to the
+                    table as it stands before round r (zeros past the end).
+    ``runs``        per sequence, the evicted logical-block ranges [x0, x1) in
+                    the order of the events that evict them.
+    ``event_pos``   per sequence, the trace index of each event.
+    ``live_len``    int32 [B] live tokens before the decoded token (L_b).
+    ``pos``         int32 [B] logical position of the decoded token (T_b).
+    ``num_pool_blocks`` physical blocks in the pool.
+    """
+    table0: np.ndarray
+    nblk0: np.ndarray
+    keeps: np.ndarray
+    runs: list
+    event_pos: list
+    live_len: np.ndarray
+    pos: np.ndarray
+    num_pool_blocks: int
+
+
+def build_decode_batch(rng: np.random.Generator, n_seqs: int,
+                       live_range=(4096, 16384), max_pos: int = 65536,
+                       events_range=(1, 6)) -> DecodeBatch:
+    """Paged caches compacted by 1-6 events, then one decode step.
+
+    Per sequence: live length ``L`` uniform on the 16-aligned values of
+    ``live_range``; event count ``K`` uniform on ``events_range``; the
+    pre-compaction length ``T`` uniform 16-aligned on ``[L + 16K, max_pos]``.
+    The ``(T-L)/16`` evicted blocks form ``K`` runs of whole blocks that never
+    touch block 0 (the prompt) or the last block; run ``r`` is removed by event
+    ``r``.  Physical ids are a seeded permutation of the pool.  The decoded
+    token sits at logical position ``T`` in a fresh block appended to the
+    table, so ``seq_len = L + 1``.
+    """
+    lo, hi = live_range
+    Ls, Ts, Ks, runs_all, evs_all = [], [], [], [], []
+    for _ in range(n_seqs):
+        L = 16 * int(rng.integers(lo // 16, hi // 16 + 1))
+        K = int(rng.integers(events_range[0], events_range[1] + 1))
+        T = 16 * int(rng.integers((L + 16 * K) // 16, max_pos // 16 + 1))
+        nb_ev = (T - L) // 16
+        nb_keep = L // 16
+        # sizes of the K evicted runs (each >= 1 block)
+        cuts = np.sort(rng.choice(np.arange(1, nb_ev), K - 1, replace=False)) \
+            if K > 1 else np.array([], dtype=np.int64)
+        sizes = np.diff(np.concatenate([[0], cuts, [nb_ev]])).astype(np.int64)
+        # K+1 gaps of kept blocks, each >= 1, summing to nb_keep
+        gcuts = np.sort(rng.choice(np.arange(1, nb_keep), K, replace=False))
+        gaps = np.diff(np.concatenate([[0], gcuts, [nb_keep]])).astype(np.int64)
+        runs, x = [], 0
+        for r in range(K):
+            x += int(gaps[r])
+            runs.append((x, x + int(sizes[r])))
+            x += int(sizes[r])
+        assert x + int(gaps[K]) == T // 16
+        # event r fires at the end of the kept gap that follows run r
+        evs = [16 * runs[r + 1][0] if r + 1 < K else T for r in range(K)]
+        Ls.append(L); Ts.append(T); Ks.append(K)
+        runs_all.append(runs); evs_all.append(evs)
+
+    nblk0 = np.array([T // 16 + 1 for T in Ts], dtype=np.int32)
+    MB = int(nblk0.max())
+    NB = int(nblk0.sum())
+    perm = rng.permutation(NB).astype(np.int32)
+    table0 = np.full((n_seqs, MB), -1, dtype=np.int32)
+    off = 0
+    for b in range(n_seqs):
+        n = int(nblk0[b])
+        table0[b, :n] = perm[off:off + n]
+        off += n
+
+    R = max(Ks)
+    keeps = np.zeros((R, n_seqs, MB), dtype=np.uint8)
+    for b in range(n_seqs):
+        logical = list(range(int(nblk0[b])))   # logical ids currently listed
+        for r in range(R):
+            if r < Ks[b]:
+                x0, x1 = runs_all[b][r]
+                flags = [0 if x0 <= x < x1 else 1 for x in logical]
+            else:
+                flags = [1] * len(logical)
+            keeps[r, b, :len(logical)] = flags
+            logical = [x for x, f in zip(logical, flags) if f]
+    return DecodeBatch(table0=table0, nblk0=nblk0, keeps=keeps,
+                       runs=runs_all, event_pos=evs_all,
+                       live_len=np.array(Ls, dtype=np.int32),
+                       pos=np.array(Ts, dtype=np.int32),
+                       num_pool_blocks=NB)
+
+
+def normal_tensor(shape, seed: int, scale: float = 1.0, dtype=None,
+                  device: str = "cpu"):
+    """N(0,1)*scale tensor, drawn in fp32 and rounded (RNE) to ``dtype`` once.
+
+    On the CPU the draw is numpy PCG64 (``default_rng(seed)``); on a GPU it is
+    torch's seeded device generator.  Either way both sides of a comparison
+    consume the same rounded values.
+    """
+    import torch
+    dtype = dtype or torch.float32
+    if str(device) == "cpu":
+        x = np.random.default_rng(seed).standard_normal(tuple(shape), dtype=np.float32)
+        t = torch.from_numpy(x)
+        if scale != 1.0:
+            t = t * scale
+        return t.to(dtype)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        t = t * scale
+    return t.to(dtype)
