@@ -1,0 +1,200 @@
+/*
+ * ks.h -- C ABI of libks.so, the KV-streams hot path for AMD MI355X (gfx950).
+ *
+ * KV-streams ("KV-streams for Efficient Compaction in Agentic Reinforcement
+ * Learning", Penaloza et al.) compacts an agent's live KV cache by splicing
+ * evicted turns out of it instead of re-prefilling a shorter sequence.  The
+ * trainer then replays the recorded compaction events as an attention mask
+ * over the continuous trace.  This library provides the GPU kernels of both
+ * sides: RoPE at logical positions, eviction-masked attention forward and
+ * backward, block-table compaction and paged GQA decode.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory      Every tensor pointer is DEVICE memory owned by the caller.  The
+ *             library never allocates: scratch space comes from a caller
+ *             workspace whose size is given by the matching *_workspace()
+ *             query.  Pointers must be 16-byte aligned.
+ * Layouts     Row-major and contiguous.  Trace tensors are [B, N, H, D]
+ *             ("BSHD"); the paged pool is [num_blocks, Hkv, 16, D].
+ * Streams     `stream` is a hipStream_t (NULL = the null stream).  Every call
+ *             is asynchronous on that stream; nothing synchronises the host.
+ * GQA         Hq % Hkv == 0; query head h reads kv head h / (Hq / Hkv).
+ * Errors      Arguments are validated before anything is launched.  A non-OK
+ *             status means nothing was written.  A launch failure returns
+ *             KS_ERR_HIP.  ks_last_error() gives a message for the last
+ *             non-OK status of the calling thread.  Nothing is printed,
+ *             thrown or aborted across the ABI.  All entry points are
+ *             reentrant; calls that share output or workspace buffers on
+ *             different streams race.
+ */
+#ifndef KS_H
+#define KS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int ks_status;
+#define KS_OK 0
+#define KS_ERR_INVALID_ARG 1
+#define KS_ERR_UNSUPPORTED 2
+#define KS_ERR_HIP 3
+#define KS_ERR_WORKSPACE 4
+
+/* element types */
+#define KS_F32 0
+#define KS_BF16 1
+
+/* e_j of a token that is never evicted */
+#define KS_NEVER 0x7fffffff
+/* tokens per paged KV block */
+#define KS_BLOCK 16
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ks_last_error(void);
+
+/* Library version string. */
+const char* ks_version(void);
+
+/*
+ * ks_rope_logical -- rotate queries and keys by their LOGICAL position.
+ *
+ * After compaction a retained key may sit in a different physical slot, but
+ * it keeps the rotation of its original position, and new queries and keys
+ * continue the original position count (KV-streams explainer on wqu.guru,
+ * the paragraph on RoPE and the one that separates physical storage from
+ * logical position).
+ *
+ * Rotate-half (NeoX) pairing: for k < D/2, theta = pos * base^(-2k/D),
+ *   x[k]       <- x[k] cos(theta) - x[k + D/2] sin(theta)
+ *   x[k + D/2] <- x[k + D/2] cos(theta) + x[k] sin(theta).
+ * The angle is formed and reduced in fp64; the rotation runs in fp32 and is
+ * rounded once to the storage type.  inverse != 0 rotates by -theta (the
+ * transpose, i.e. the backward of the rotation).
+ *
+ * q    [B, N, Hq, D]  in place (may be NULL when Hq == 0 or q is not wanted)
+ * k    [B, N, Hkv, D] in place (may be NULL likewise)
+ * pos  int32 [B, N]   logical positions (device)
+ * dtype KS_F32 or KS_BF16; D even, 2 <= D <= 256, D % 16 == 0.
+ */
+ks_status ks_rope_logical(void* q, void* k, const int32_t* pos, int B, int N,
+                          int Hq, int Hkv, int D, int dtype, float base,
+                          int inverse, void* stream);
+
+/*
+ * ks_evict_attn_fwd -- attention over a continuous trace under the eviction
+ * mask that reproduces compaction.
+ *
+ * The trainer replays every recorded compaction event: retained tokens keep
+ * the states they formed before compaction, later tokens cannot attend spans
+ * that inference had already removed (explainer, trainer paragraph; paper
+ * page, Fig. 2A: "an attention mask that reproduces eviction").  With e_j the
+ * trace index of the event that evicted token j (KS_NEVER if never):
+ *   M_ij = [j <= i] and [i < e_j]
+ *   LSE_i = log sum_{j: M_ij} exp(scale q_i.k_j)
+ *   O_i   = sum_{j: M_ij} exp(scale q_i.k_j - LSE_i) v_j
+ * Key tiles that no query of a tile can see are skipped using the per-tile
+ * minimum and maximum of e.
+ *
+ * q    [B, N, Hq, D]   (rotated; dtype)
+ * k, v [B, N, Hkv, D]  (k rotated; dtype)
+ * e    int32 [B, N]    must satisfy e_j > j; any value >= N means "never"
+ * o    [B, N, Hq, D]   output (dtype)
+ * lse  float [B, Hq, N] output, natural log, may be NULL
+ * dtype KS_BF16 (D = 128 or 64, fp32 accumulation) or KS_F32 (D <= 128,
+ *       D % 16 == 0).
+ * ws   workspace of at least ks_evict_attn_fwd_workspace() bytes.
+ */
+size_t ks_evict_attn_fwd_workspace(int B, int N, int Hq, int Hkv, int D,
+                                   int dtype);
+ks_status ks_evict_attn_fwd(const void* q, const void* k, const void* v,
+                            const int32_t* e, void* o, float* lse, int B,
+                            int N, int Hq, int Hkv, int D, int dtype,
+                            float scale, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
+ * ks_evict_attn_bwd -- gradients of ks_evict_attn_fwd.
+ *
+ * Softmax backward over the same mask (the pages state none; this is the
+ * calculus of the forward above):
+ *   P = exp(S - LSE), dV_j = sum_i P_ij dO_i, dP_ij = dO_i.v_j,
+ *   D_i = sum_j P_ij dP_ij = dO_i.O_i, dS = P (dP - D_i),
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
+ * dK and dV sum over the query heads that share a kv head.  Gradients are
+ * with respect to the rotated q and k (apply ks_rope_logical with inverse=1
+ * to obtain gradients of the raw projections).  Deterministic: no atomics.
+ *
+ * o, lse  outputs of the forward on the same inputs (lse required)
+ * dout    [B, N, Hq, D] upstream gradient (dtype)
+ * dq      [B, N, Hq, D], dk, dv [B, N, Hkv, D] outputs (dtype)
+ * dtype   KS_BF16 with D = 128.
+ */
+size_t ks_evict_attn_bwd_workspace(int B, int N, int Hq, int Hkv, int D,
+                                   int dtype);
+ks_status ks_evict_attn_bwd(const void* q, const void* k, const void* v,
+                            const int32_t* e, const void* o, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv,
+                            int B, int N, int Hq, int Hkv, int D, int dtype,
+                            float scale, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
+ * ks_compact_block_table -- splice evicted blocks out of paged block tables.
+ *
+ * The table may not keep empty slots, so complete blocks are removed and the
+ * remaining block references are joined, order preserved (explainer, the
+ * paragraph on vLLM's 16-token blocks and the block table):
+ *   out_b = [table_b[x] for x < nblk_in_b if keep_b[x]],  nblk_out_b = |out_b|,
+ *   out_b[x] = -1 for x >= nblk_out_b.
+ * If pos_in is given, the same selection is applied to it (e.g. the logical
+ * index of each block) into pos_out.
+ *
+ * table_in, table_out  int32 [B, max_blocks] (device; must not alias)
+ * nblk_in, nblk_out    int32 [B] (device; may alias each other); entries of
+ *                      nblk_in are clamped to [0, max_blocks]
+ * keep                 uint8 [B, max_blocks], nonzero = keep
+ * pos_in, pos_out      int32 [B, max_blocks] or both NULL
+ */
+ks_status ks_compact_block_table(const int32_t* table_in,
+                                 const int32_t* nblk_in, const uint8_t* keep,
+                                 int32_t* table_out, int32_t* nblk_out,
+                                 const int32_t* pos_in, int32_t* pos_out,
+                                 int B, int max_blocks, void* stream);
+
+/*
+ * ks_paged_decode -- one GQA decode step over compacted paged caches.
+ *
+ * Each sequence attends the first seq_lens[b] tokens reached through its
+ * block table.  Keys in the pool were rotated at their own logical positions
+ * when written, and q was rotated at the decoded token's logical position, so
+ * attention over the spliced table equals the trainer's masked attention row
+ * for that token (explainer: RoPE and block-table paragraphs).
+ *
+ * q        [B, Hq, D] bf16 (rotated)
+ * k_pool,
+ * v_pool   [num_pool_blocks, Hkv, 16, D] bf16
+ * table    int32 [B, max_blocks]; entries < ceil(seq_lens[b] / 16) must be
+ *          valid pool indices; an out-of-range id makes that sequence's
+ *          output NaN (nothing outside the pool is read)
+ * seq_lens int32 [B], 0 <= seq_lens[b] <= 16 * max_blocks; a zero-length
+ *          sequence yields a zero output and lse = -inf
+ * out      [B, Hq, D] bf16;  lse float [B, Hq] natural log, may be NULL
+ * dtype    KS_BF16; D = 128.
+ */
+size_t ks_paged_decode_workspace(int B, int Hq, int D, int max_blocks);
+ks_status ks_paged_decode(const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* table,
+                          const int32_t* seq_lens, void* out, float* lse,
+                          int B, int Hq, int Hkv, int D, int max_blocks,
+                          int num_pool_blocks, int dtype, float scale,
+                          void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KS_H */

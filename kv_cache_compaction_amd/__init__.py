@@ -1,0 +1,13 @@
+"""KV-streams hot path on AMD MI355X (gfx950): Python binding of libks.so.
+
+The kernels (RoPE at logical positions, eviction-masked attention forward and
+backward, block-table compaction, paged GQA decode) live in libks.so, built
+from ``csrc/`` by ``python -m kv_cache_compaction_amd.build``.  This package
+only marshals torch tensors into the C ABI declared in ``include/ks.h``.
+"""
+from ._lib import (  # noqa: F401
+    KS_BF16, KS_BLOCK, KS_F32, KS_NEVER, KSError, LIB_PATH, header_functions,
+    ks_compact_block_table, ks_evict_attn_bwd, ks_evict_attn_bwd_workspace,
+    ks_evict_attn_fwd, ks_evict_attn_fwd_workspace, ks_paged_decode,
+    ks_paged_decode_workspace, ks_rope_logical, load_library,
+)

@@ -1,0 +1,252 @@
+"""ctypes binding of libks.so.
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels.  torch provides device memory (outputs and workspaces) and the
+current stream.  If libks.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libks.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "ks.h")
+
+KS_OK = 0
+KS_F32 = 0
+KS_BF16 = 1
+KS_NEVER = 0x7FFFFFFF
+KS_BLOCK = 16
+
+_STATUS = {1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "HIP_ERROR", 4: "WORKSPACE_TOO_SMALL"}
+
+
+class KSError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "ks_last_error": ([], ctypes.c_char_p),
+    "ks_version": ([], ctypes.c_char_p),
+    "ks_rope_logical": ([_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp], _i),
+    "ks_evict_attn_fwd_workspace": ([_i, _i, _i, _i, _i, _i], _sz),
+    "ks_evict_attn_fwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz,
+                           _vp], _i),
+    "ks_evict_attn_bwd_workspace": ([_i, _i, _i, _i, _i, _i], _sz),
+    "ks_evict_attn_bwd": ([_vp] * 10 + [_i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+    "ks_compact_block_table": ([_vp] * 7 + [_i, _i, _vp], _i),
+    "ks_paged_decode_workspace": ([_i, _i, _i, _i], _sz),
+    "ks_paged_decode": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libks.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} not found: build it with `python -m kv_cache_compaction_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions declared in include/ks.h."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ks_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(fn, st):
+    if st != KS_OK:
+        msg = load_library().ks_last_error().decode(errors="replace")
+        raise KSError(fn, st, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return KS_F32
+    if t.dtype == torch.bfloat16:
+        return KS_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _cuda_contig(name, t, dtype=None):
+    _need(t.is_cuda, f"{name} must be a GPU tensor")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _workspace(nbytes, device, ws):
+    if ws is None:
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    _need(ws.numel() * ws.element_size() >= nbytes, "workspace too small")
+    return ws
+
+
+# ---------------------------------------------------------------------------
+def ks_rope_logical(q, k, pos, base=10000.0, inverse=False, stream=None):
+    """Rotate q [B,N,Hq,D] and/or k [B,N,Hkv,D] in place at positions pos [B,N]."""
+    lib = load_library()
+    ref = q if q is not None else k
+    _need(ref is not None, "q or k required")
+    B, N, _, D = ref.shape
+    for name, t in (("q", q), ("k", k)):
+        if t is not None:
+            _cuda_contig(name, t, ref.dtype)
+            _need(t.shape[0] == B and t.shape[1] == N and t.shape[3] == D, f"{name} shape")
+    _cuda_contig("pos", pos, torch.int32)
+    _need(tuple(pos.shape) == (B, N), "pos must be [B, N]")
+    Hq = q.shape[2] if q is not None else 0
+    Hkv = k.shape[2] if k is not None else 0
+    st = lib.ks_rope_logical(_ptr(q), _ptr(k), _ptr(pos), B, N, Hq, Hkv, D, _dtype_code(ref),
+                             float(base), int(bool(inverse)), _stream(stream))
+    _check("ks_rope_logical", st)
+    return q, k
+
+
+def ks_evict_attn_fwd_workspace(B, N, Hq, Hkv, D, dtype_code):
+    return load_library().ks_evict_attn_fwd_workspace(B, N, Hq, Hkv, D, dtype_code)
+
+
+def ks_evict_attn_fwd(q, k, v, e, scale=None, out=None, lse=None, ws=None, stream=None):
+    """Eviction-masked attention forward.  Returns (o, lse)."""
+    lib = load_library()
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _cuda_contig("q", q)
+    _cuda_contig("k", k, q.dtype)
+    _cuda_contig("v", v, q.dtype)
+    _cuda_contig("e", e, torch.int32)
+    _need(tuple(k.shape) == (B, N, Hkv, D) and tuple(v.shape) == (B, N, Hkv, D), "k/v shape")
+    _need(tuple(e.shape) == (B, N), "e must be [B, N]")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _cuda_contig("out", out, q.dtype)
+    _cuda_contig("lse", lse, torch.float32)
+    code = _dtype_code(q)
+    nbytes = lib.ks_evict_attn_fwd_workspace(B, N, Hq, Hkv, D, code)
+    ws = _workspace(nbytes, q.device, ws)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.ks_evict_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(out), _ptr(lse), B, N, Hq,
+                               Hkv, D, code, sc, _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream))
+    _check("ks_evict_attn_fwd", st)
+    return out, lse
+
+
+def ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, dtype_code):
+    return load_library().ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, dtype_code)
+
+
+def ks_evict_attn_bwd(q, k, v, e, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None,
+                      stream=None):
+    """Gradients of the masked forward.  Returns (dq, dk, dv)."""
+    lib = load_library()
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _cuda_contig(name, t, q.dtype)
+    _cuda_contig("e", e, torch.int32)
+    _cuda_contig("lse", lse, torch.float32)
+    _need(tuple(o.shape) == tuple(q.shape) and tuple(dout.shape) == tuple(q.shape), "o/dout")
+    _need(tuple(lse.shape) == (B, Hq, N), "lse must be [B, Hq, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    code = _dtype_code(q)
+    nbytes = lib.ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, code)
+    ws = _workspace(nbytes, q.device, ws)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.ks_evict_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(o), _ptr(lse),
+                               _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, N, Hq, Hkv, D, code,
+                               sc, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("ks_evict_attn_bwd", st)
+    return dq, dk, dv
+
+
+def ks_compact_block_table(table_in, nblk_in, keep, table_out=None, nblk_out=None, pos_in=None,
+                           pos_out=None, stream=None):
+    """Splice dropped blocks out of each table row.  Returns (table_out, nblk_out, pos_out)."""
+    lib = load_library()
+    B, MB = table_in.shape
+    _cuda_contig("table_in", table_in, torch.int32)
+    _cuda_contig("nblk_in", nblk_in, torch.int32)
+    _cuda_contig("keep", keep, torch.uint8)
+    _need(tuple(keep.shape) == (B, MB) and tuple(nblk_in.shape) == (B,), "keep/nblk shape")
+    table_out = torch.empty_like(table_in) if table_out is None else table_out
+    nblk_out = torch.empty_like(nblk_in) if nblk_out is None else nblk_out
+    if pos_in is not None and pos_out is None:
+        pos_out = torch.empty_like(pos_in)
+    st = lib.ks_compact_block_table(_ptr(table_in), _ptr(nblk_in), _ptr(keep), _ptr(table_out),
+                                    _ptr(nblk_out), _ptr(pos_in), _ptr(pos_out), B, MB,
+                                    _stream(stream))
+    _check("ks_compact_block_table", st)
+    return table_out, nblk_out, pos_out
+
+
+def ks_paged_decode_workspace(B, Hq, D, max_blocks):
+    return load_library().ks_paged_decode_workspace(B, Hq, D, max_blocks)
+
+
+def ks_paged_decode(q, k_pool, v_pool, table, seq_lens, scale=None, out=None, lse=None, ws=None,
+                    stream=None):
+    """One GQA decode step over paged caches.  Returns (out, lse)."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    NB, Hkv, BS, _ = k_pool.shape
+    _need(BS == KS_BLOCK, "pool block size must be 16")
+    _cuda_contig("q", q)
+    _cuda_contig("k_pool", k_pool, q.dtype)
+    _cuda_contig("v_pool", v_pool, q.dtype)
+    _cuda_contig("table", table, torch.int32)
+    _cuda_contig("seq_lens", seq_lens, torch.int32)
+    _need(tuple(v_pool.shape) == tuple(k_pool.shape), "v_pool shape")
+    _need(table.shape[0] == B and tuple(seq_lens.shape) == (B,), "table/seq_lens shape")
+    MB = table.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    nbytes = lib.ks_paged_decode_workspace(B, Hq, D, max(MB, 1))
+    ws = _workspace(nbytes, q.device, ws)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.ks_paged_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(table), _ptr(seq_lens),
+                             _ptr(out), _ptr(lse), B, Hq, Hkv, D, MB, NB, _dtype_code(q), sc,
+                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("ks_paged_decode", st)
+    return out, lse

@@ -1,0 +1,575 @@
+// Backward of the eviction-masked attention (bf16, D = 128).
+//
+// The mask replays compaction (KV-streams explainer, trainer paragraph;
+// paper page, Fig. 2A); the gradients follow from the softmax calculus:
+//   P = exp(S - LSE), dV = P^T dO, dP = dO V^T, D_i = rowsum(dO o O),
+//   dS = P o (dP - D_i), dQ = scale dS K, dK = scale dS^T Q.
+//
+// Deterministic two-kernel split (no atomics, no fp32 dQ workspace):
+//   dkdv_kernel  key-tile outer.  A workgroup owns 128 keys of one kv head
+//                (32 per wave, K and V held in registers as MFMA operands)
+//                and walks every query head of the group over the query
+//                rows that can see those keys, [j0, max e_j).  Per 32-query
+//                chunk staged in LDS (natural and transposed): S = Q K^T,
+//                dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS  (4 MFMA GEMMs).
+//   dq_kernel    query-tile outer, laid out like the forward (64 rows per
+//                wave, key tiles staged in LDS, live tiles found by ballot):
+//                S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (3 GEMMs).
+// The pair executes 14*D flops per live (query, key, head) triple against
+// the 10*D of a fused kernel, in exchange for no atomic traffic at all.
+#include "attn_common.h"
+
+namespace ksattn {
+namespace {
+
+constexpr int D = 128;
+constexpr int NSTEP = D / 16;  // k-steps over the head dimension
+constexpr int NDB = D / 32;    // 32-wide d blocks
+constexpr int CH = D / 8;      // 16-byte chunks per row
+
+// ---------------------------------------------------------------------------
+// D_i = sum_d dO_id O_id  (fp32), and LSE in log2 units
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ o,
+                                                      const bf16_t* __restrict__ dout,
+                                                      float* __restrict__ di, long long rows,
+                                                      int N, int Hq) {
+  // 16 threads per (b, i, h) row of D = 128 values
+  const long long r = static_cast<long long>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  float acc = 0.f;
+  if (r < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + r * D + c * 8);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dout + r * D + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc += lo_bf16(a[i]) * lo_bf16(g[i]) + hi_bf16(a[i]) * hi_bf16(g[i]);
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (r < rows && c == 0) {
+    // r = (b * N + i) * Hq + h  ->  di[(b * Hq + h) * N + i]
+    const long long h = r % Hq;
+    const long long bi = r / Hq;
+    const long long b = bi / N, i = bi % N;
+    di[(b * Hq + h) * N + i] = acc;
+  }
+}
+
+// slot of the first of 4 consecutive rows (4*g) in the MFMA k order: bits 2
+// and 3 of the row index swapped within each 16-row group
+__device__ __forceinline__ int quad_slot(int g) {
+  return 16 * (g >> 2) + 8 * (g & 1) + 4 * ((g >> 1) & 1);
+}
+
+// 4 rows x 8 bf16 (u32x4 each) -> for column dd, the 4 values as 2 packed words
+__device__ __forceinline__ u32x2 column4(const u32x4 (&x)[4], int dd) {
+  const int ws = dd >> 1;
+  if (dd & 1)
+    return u32x2{(x[0][ws] >> 16) | (x[1][ws] & 0xffff0000u),
+                 (x[2][ws] >> 16) | (x[3][ws] & 0xffff0000u)};
+  return u32x2{(x[0][ws] & 0xffffu) | (x[1][ws] << 16), (x[2][ws] & 0xffffu) | (x[3][ws] << 16)};
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: key-tile outer
+// ---------------------------------------------------------------------------
+constexpr int KW = 128;  // keys per workgroup (4 waves x 32)
+constexpr int BQ = 32;   // query rows per chunk
+
+__global__ __launch_bounds__(256) void dkdv_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
+    const int32_t* __restrict__ emax, const float* __restrict__ lse,
+    const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk,
+    bf16_t* __restrict__ dv, int B, int N, int Hq, int Hkv, int ntiles, int nkt, int total_wg,
+    float scale) {
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Os[2][BQ * D];   // dO natural
+  __shared__ __attribute__((aligned(16))) bf16_t Qt[2][D * BQ];
+  __shared__ __attribute__((aligned(16))) bf16_t Ot[2][D * BQ];   // dO transposed
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+
+  int lin = blockIdx.x;
+  lin = (lin & 7) * (total_wg >> 3) + (lin >> 3);
+  if (lin >= B * Hkv * nkt) return;
+  const int kt = lin % nkt;
+  const int hkv = (lin / nkt) % Hkv;
+  const int b = lin / (nkt * Hkv);
+  const int G = Hq / Hkv;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, lh = lane >> 5;
+  const int j0 = kt * KW;
+  const int kw0 = j0 + 32 * w;
+  const int jl = kw0 + lq;  // this lane's key
+  const size_t tokkv = static_cast<size_t>(Hkv) * D;
+  const size_t tokq = static_cast<size_t>(Hq) * D;
+
+  // K^T / V^T as B operands: lane holds row jl, d = 16*step + 8*lh .. +8
+  bf16x8 kf[NSTEP], vf[NSTEP];
+  {
+    const size_t off = (static_cast<size_t>(b) * N + (jl < N ? jl : 0)) * tokkv +
+                       static_cast<size_t>(hkv) * D + lh * 8;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      u32x4 a = *reinterpret_cast<const u32x4*>(k + off + s * 16);
+      u32x4 c = *reinterpret_cast<const u32x4*>(v + off + s * 16);
+      if (jl >= N) a = c = u32x4{0u, 0u, 0u, 0u};
+      kf[s] = __builtin_bit_cast(bf16x8, a);
+      vf[s] = __builtin_bit_cast(bf16x8, c);
+    }
+  }
+  const int ej = jl < N ? e[static_cast<size_t>(b) * N + jl] : 0;
+
+  // query range of the workgroup and of this wave
+  const int t0 = j0 / kKeyTile;
+  const int t1 = min(ntiles - 1, t0 + KW / kKeyTile - 1);
+  int emx = 0x80000000, emn = 0x7fffffff;
+  for (int t = t0; t <= t1; ++t) {
+    emx = max(emx, emax[static_cast<size_t>(b) * ntiles + t]);
+    emn = min(emn, emin[static_cast<size_t>(b) * ntiles + t]);
+  }
+  const int qend = min(N, emx);  // exclusive
+  // wave-level range (uniform): keys [kw0, kw0 + 32), max e over them
+  int wemx = jl < N ? ej : static_cast<int>(0x80000000);
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) wemx = max(wemx, __shfl_xor(wemx, off));
+  const int wq1 = min(N, wemx);
+  const int kmax = min(N, j0 + KW) - 1;  // last existing key of the workgroup
+
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dka[db][r] = dva[db][r] = 0.f;
+
+  const float sl2 = scale * KS_LOG2E;
+  // staging registers: threads 0..127 handle Q, 128..255 handle dO; each a
+  // (4-row group, 16-byte d chunk) pair
+  const int half = tid >> 7;
+  const int pr = tid & 127;
+  const int qg = pr & 7, dc = pr >> 3;
+  u32x4 xr[4];
+  float lr = 0.f;
+
+  const int c_begin = j0 / BQ;
+  const int c_end = (qend + BQ - 1) / BQ;  // exclusive
+  const int nchunks = c_end > c_begin ? (c_end - c_begin) * G : 0;
+
+  auto load_chunk = [&](int idx) {
+    const int h = hkv * G + idx / (c_end - c_begin);
+    const int c0 = (c_begin + idx % (c_end - c_begin)) * BQ;
+    const bf16_t* src = half ? dout : q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = c0 + 4 * qg + i;
+      xr[i] = row < N ? *reinterpret_cast<const u32x4*>(
+                            src + (static_cast<size_t>(b) * N + row) * tokq +
+                            static_cast<size_t>(h) * D + dc * 8)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < 2 * BQ) {
+      const int row = c0 + (tid & (BQ - 1));
+      const size_t li = (static_cast<size_t>(b) * Hq + h) * N + row;
+      if (tid < BQ)
+        lr = row < N ? lse[li] * KS_LOG2E : INFINITY;
+      else
+        lr = row < N ? di[li] : 0.f;
+    }
+  };
+  auto store_chunk = [&](int buf) {
+    bf16_t* nat = half ? Os[buf] : Qs[buf];
+    bf16_t* tr = half ? Ot[buf] : Qt[buf];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * qg + i;
+      *reinterpret_cast<u32x4*>(&nat[row * D + ((dc ^ (row & (CH - 1))) * 8)]) = xr[i];
+    }
+    const int slot = quad_slot(qg);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const int d = dc * 8 + dd;
+      const int chunk = (slot >> 3) ^ ((d >> 2) & 3);
+      *reinterpret_cast<u32x2*>(&tr[d * BQ + chunk * 8 + (slot & 7)]) = column4(xr, dd);
+    }
+    if (tid < BQ)
+      Ls[buf][tid] = lr;
+    else if (tid < 2 * BQ)
+      Ds[buf][tid - BQ] = lr;
+  };
+
+  auto compute = [&](int buf, int c0) {
+    // skip chunks none of this wave's keys can see (uniform per wave)
+    if (c0 >= wq1 || c0 + BQ <= kw0) return;
+    const bool full = (c0 >= kmax) && (c0 + BQ <= emn) && (c0 + BQ <= N);
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      const int c = 2 * s + lh;
+      const int off = lq * D + ((c ^ (lq & (CH - 1))) * 8);
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&Qs[buf][off]);
+      const bf16x8 gf = *reinterpret_cast<const bf16x8*>(&Os[buf][off]);
+      sacc = mfma32x32x16(af, kf[s], sacc);  // S[q][key]:  lane col = key
+      pacc = mfma32x32x16(gf, vf[s], pacc);  // dP[q][key]
+    }
+    bf16x8 pf[2], sf[2];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int ql = rg * 8 + lh * 4;
+      const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][ql]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&Ds[buf][ql]);
+      const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = rg * 4 + c;
+        float p = fast_exp2(sacc[r] * sl2 - la[c]);
+        if (!full) {
+          const int i = c0 + ql + c;
+          const bool live = jl <= i && i < ej && i < N && jl < N;
+          p = live ? p : 0.f;
+        }
+        const float ds = p * (pacc[r] - da[c]);
+        pf[r >> 3][r & 7] = (__bf16)p;
+        sf[r >> 3][r & 7] = (__bf16)ds;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 32 + lq;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int chunk = (2 * ks + lh) ^ ((d >> 2) & 3);
+        const bf16x8 of = *reinterpret_cast<const bf16x8*>(&Ot[buf][d * BQ + chunk * 8]);
+        const bf16x8 qtf = *reinterpret_cast<const bf16x8*>(&Qt[buf][d * BQ + chunk * 8]);
+        dva[db] = mfma32x32x16(of, pf[ks], dva[db]);   // dV^T[d][key]
+        dka[db] = mfma32x32x16(qtf, sf[ks], dka[db]);  // dK^T[d][key]
+      }
+    }
+  };
+
+  if (nchunks > 0) {
+    load_chunk(0);
+    store_chunk(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int idx = 0; idx < nchunks; ++idx) {
+    const bool more = idx + 1 < nchunks;
+    if (more) load_chunk(idx + 1);
+    compute(buf, (c_begin + idx % (c_end - c_begin)) * BQ);
+    if (more) store_chunk(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // epilogue: lane holds key jl; rows of dK^T/dV^T are d = 32db + 8rg + 4lh + c
+  if (jl < N) {
+    const size_t off = (static_cast<size_t>(b) * N + jl) * tokkv + static_cast<size_t>(hkv) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = db * 32 + rg * 8 + lh * 4;
+        const u32x2 kw = {pack_bf16x2(dka[db][rg * 4] * scale, dka[db][rg * 4 + 1] * scale),
+                          pack_bf16x2(dka[db][rg * 4 + 2] * scale, dka[db][rg * 4 + 3] * scale)};
+        const u32x2 vw = {pack_bf16x2(dva[db][rg * 4], dva[db][rg * 4 + 1]),
+                          pack_bf16x2(dva[db][rg * 4 + 2], dva[db][rg * 4 + 3])};
+        *reinterpret_cast<u32x2*>(dk + off + d) = kw;
+        *reinterpret_cast<u32x2*>(dv + off + d) = vw;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query-tile outer
+// ---------------------------------------------------------------------------
+constexpr int KT = kKeyTile;
+
+template <int HPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dq_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
+    const int32_t* __restrict__ emax, const float* __restrict__ lse,
+    const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
+    int B, int N, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale) {
+  constexpr int RS = 4 / HPW;
+  constexpr int BM = 64 * RS;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Kt[2][D * KT];
+  __shared__ __attribute__((aligned(16))) int Es[2][KT];
+
+  int lin = blockIdx.x;
+  lin = (lin & 7) * (total_wg >> 3) + (lin >> 3);
+  const int ngrp = Hq / HPW;
+  if (lin >= B * ngrp * nqt) return;
+  const int qt = lin % nqt;
+  const int grp = (lin / nqt) % ngrp;
+  const int b = lin / (nqt * ngrp);
+  const int G = Hq / Hkv;
+  const int hq0 = grp * HPW;
+  const int hkv = hq0 / G;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int hq = hq0 + (w % HPW);
+  const int i0 = qt * BM;
+  const int wi0 = i0 + (w / HPW) * 64;
+  const int i1 = min(N, i0 + BM);
+  const int lq = lane & 31, lh = lane >> 5;
+  const size_t tokkv = static_cast<size_t>(Hkv) * D;
+  const size_t tokq = static_cast<size_t>(Hq) * D;
+  const bf16_t* kb = k + static_cast<size_t>(b) * N * tokkv + static_cast<size_t>(hkv) * D;
+  const bf16_t* vb = v + static_cast<size_t>(b) * N * tokkv + static_cast<size_t>(hkv) * D;
+  const int32_t* eb = e + static_cast<size_t>(b) * N;
+  const int32_t* eminb = emin + static_cast<size_t>(b) * ntiles;
+  const float sl2 = scale * KS_LOG2E;
+
+  bf16x8 qf[2][NSTEP], gf[2][NSTEP];
+  float l2[2], dii[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = wi0 + qb * 32 + lq;
+    const size_t off = (static_cast<size_t>(b) * N + (row < N ? row : 0)) * tokq +
+                       static_cast<size_t>(hq) * D + lh * 8;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      u32x4 a = *reinterpret_cast<const u32x4*>(q + off + s * 16);
+      u32x4 c = *reinterpret_cast<const u32x4*>(dout + off + s * 16);
+      if (row >= N) a = c = u32x4{0u, 0u, 0u, 0u};
+      qf[qb][s] = __builtin_bit_cast(bf16x8, a);
+      gf[qb][s] = __builtin_bit_cast(bf16x8, c);
+    }
+    const size_t li = (static_cast<size_t>(b) * Hq + hq) * N + (row < N ? row : 0);
+    l2[qb] = row < N ? lse[li] * KS_LOG2E : INFINITY;
+    dii[qb] = row < N ? di[li] : 0.f;
+  }
+  f32x16 dqa[2][NDB];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqa[qb][db][r] = 0.f;
+
+  // staging: thread = (4-key group kg, d chunk dc) pair; 16 x 16 = 256 pairs
+  const int kg = tid & 15, dc = tid >> 4;
+  u32x4 kr[4], vr[4];
+  int er = 0;
+  auto load_tile = [&](int t) {
+    const int j0 = t * KT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 4 * kg + i;
+      const bool ok = j < N;
+      kr[i] = ok ? *reinterpret_cast<const u32x4*>(kb + j * tokkv + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+      vr[i] = ok ? *reinterpret_cast<const u32x4*>(vb + j * tokkv + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < KT) er = (j0 + tid < N) ? eb[j0 + tid] : 0;
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * kg + i;
+      const int o = row * D + ((dc ^ (row & (CH - 1))) * 8);
+      *reinterpret_cast<u32x4*>(&Ks[buf][o]) = kr[i];
+      *reinterpret_cast<u32x4*>(&Vs[buf][o]) = vr[i];
+    }
+    const int slot = quad_slot(kg);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const int d = dc * 8 + dd;
+      const int chunk = (slot >> 3) ^ ((d >> 1) & 7);
+      *reinterpret_cast<u32x2*>(&Kt[buf][d * KT + chunk * 8 + (slot & 7)]) = column4(kr, dd);
+    }
+    if (tid < KT) Es[buf][tid] = er;
+  };
+
+  auto compute = [&](int buf, int j0, bool partial) {
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk) {
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[0][r] = sacc[1][r] = pacc[0][r] = pacc[1][r] = 0.f;
+      const int krow = kbk * 32 + lq;
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        const int c = 2 * s + lh;
+        const int off = krow * D + ((c ^ (krow & (CH - 1))) * 8);
+        const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&Ks[buf][off]);
+        const bf16x8 vfr = *reinterpret_cast<const bf16x8*>(&Vs[buf][off]);
+        sacc[0] = mfma32x32x16(kfr, qf[0][s], sacc[0]);  // S^T[key][q]
+        sacc[1] = mfma32x32x16(kfr, qf[1][s], sacc[1]);
+        pacc[0] = mfma32x32x16(vfr, gf[0][s], pacc[0]);  // dP^T[key][q]
+        pacc[1] = mfma32x32x16(vfr, gf[1][s], pacc[1]);
+      }
+      bf16x8 sf[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int i = wi0 + qb * 32 + lq;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int kl = kbk * 32 + rg * 8 + lh * 4;
+          int ee[4] = {0, 0, 0, 0};
+          if (partial) {
+            const int4 ev = *reinterpret_cast<const int4*>(&Es[buf][kl]);
+            ee[0] = ev.x;
+            ee[1] = ev.y;
+            ee[2] = ev.z;
+            ee[3] = ev.w;
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = rg * 4 + c;
+            float p = fast_exp2(sacc[qb][r] * sl2 - l2[qb]);
+            if (partial) {
+              const int j = j0 + kl + c;
+              const bool live = j <= i && i < ee[c] && j < N;
+              p = live ? p : 0.f;
+            }
+            sf[qb][r >> 3][r & 7] = (__bf16)(p * (pacc[qb][r] - dii[qb]));
+          }
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = db * 32 + lq;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int chunk = (4 * kbk + 2 * ks + lh) ^ ((d >> 1) & 7);
+          const bf16x8 ktf = *reinterpret_cast<const bf16x8*>(&Kt[buf][d * KT + chunk * 8]);
+          dqa[0][db] = mfma32x32x16(ktf, sf[0][ks], dqa[0][db]);  // dQ^T[d][q]
+          dqa[1][db] = mfma32x32x16(ktf, sf[1][ks], dqa[1][db]);
+        }
+      }
+    }
+  };
+
+  LiveTiles it;
+  it.init(emax + static_cast<size_t>(b) * ntiles, (i1 - 1) / KT, i0);
+  int t = it.next();
+  if (t >= 0) {
+    load_tile(t);
+    store_tile(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (t >= 0) {
+    const int tn = it.next();
+    if (tn >= 0) load_tile(tn);
+    const int j0 = t * KT;
+    const bool full = (j0 + KT - 1 <= i0) && (eminb[t] >= i1) && (j0 + KT <= N);
+    compute(buf, j0, !full);
+    if (tn >= 0) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    t = tn;
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int i = wi0 + qb * 32 + lq;
+    if (i < N) {
+      bf16_t* op = dq + (static_cast<size_t>(b) * N + i) * tokq + static_cast<size_t>(hq) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d = db * 32 + rg * 8 + lh * 4;
+          const f32x16& a = dqa[qb][db];
+          *reinterpret_cast<u32x2*>(op + d) =
+              u32x2{pack_bf16x2(a[rg * 4] * scale, a[rg * 4 + 1] * scale),
+                    pack_bf16x2(a[rg * 4 + 2] * scale, a[rg * 4 + 3] * scale)};
+        }
+    }
+  }
+}
+
+size_t di_bytes(int B, int N, int Hq) {
+  return (static_cast<size_t>(B) * Hq * N * sizeof(float) + 255) & ~static_cast<size_t>(255);
+}
+
+}  // namespace
+}  // namespace ksattn
+
+using namespace ksattn;
+
+extern "C" size_t ks_evict_attn_bwd_workspace(int B, int N, int Hq, int Hkv, int Dh, int dtype) {
+  (void)Hkv;
+  (void)Dh;
+  (void)dtype;
+  if (B <= 0 || N <= 0 || Hq <= 0) return 0;
+  return summary_bytes(B, N) + di_bytes(B, N, Hq);
+}
+
+extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void* v,
+                                       const int32_t* e, const void* o, const float* lse,
+                                       const void* dout, void* dq, void* dk, void* dv, int B,
+                                       int N, int Hq, int Hkv, int Dh, int dtype, float scale,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  KS_REQUIRE(B >= 0 && N >= 0 && Hq > 0 && Hkv > 0, "ks_evict_attn_bwd: bad sizes");
+  KS_REQUIRE(Hq % Hkv == 0, "ks_evict_attn_bwd: Hq %% Hkv != 0");
+  if (dtype != KS_BF16 || Dh != D)
+    return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_bwd: only bf16 with D=128 (dtype=%d D=%d)",
+                   dtype, Dh);
+  const int G = Hq / Hkv;
+  const int hpw = G >= 4 ? 4 : G;
+  if (G % hpw != 0)
+    return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_bwd: group size %d unsupported", G);
+  if (B == 0 || N == 0) return KS_OK;
+  KS_REQUIRE(q && k && v && e && o && lse && dout && dq && dk && dv,
+             "ks_evict_attn_bwd: null pointer");
+  KS_REQUIRE(ks_aligned16(q) && ks_aligned16(k) && ks_aligned16(v) && ks_aligned16(o) &&
+                 ks_aligned16(dout) && ks_aligned16(dq) && ks_aligned16(dk) && ks_aligned16(dv),
+             "ks_evict_attn_bwd: tensors must be 16-byte aligned");
+  const size_t need = summary_bytes(B, N) + di_bytes(B, N, Hq);
+  if (!ws || ws_bytes < need)
+    return ks_fail(KS_ERR_WORKSPACE, "ks_evict_attn_bwd: workspace %zu < %zu bytes", ws_bytes,
+                   need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t *emin, *emax;
+  ks_status st = launch_summary(e, ws, B, N, s, &emin, &emax);
+  if (st != KS_OK) return st;
+  float* di = reinterpret_cast<float*>(static_cast<char*>(ws) + summary_bytes(B, N));
+  const int ntiles = (N + kKeyTile - 1) / kKeyTile;
+  const bf16_t* qq = static_cast<const bf16_t*>(q);
+  const bf16_t* kk = static_cast<const bf16_t*>(k);
+  const bf16_t* vv = static_cast<const bf16_t*>(v);
+  const bf16_t* gg = static_cast<const bf16_t*>(dout);
+
+  const long long rows = static_cast<long long>(B) * N * Hq;
+  KS_REQUIRE((rows + 15) / 16 < (1LL << 31), "ks_evict_attn_bwd: too many rows");
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0,
+                     s, static_cast<const bf16_t*>(o), gg, di, rows, N, Hq);
+  st = ks_check_launch("ks_evict_attn_bwd(pre)");
+  if (st != KS_OK) return st;
+
+  const int nkt = (N + KW - 1) / KW;
+  const long long real_kv = static_cast<long long>(B) * Hkv * nkt;
+  const long long total_kv = (real_kv + 7) / 8 * 8;
+  KS_REQUIRE(total_kv < (1LL << 31), "ks_evict_attn_bwd: grid too large");
+  hipLaunchKernelGGL(dkdv_kernel, dim3(static_cast<unsigned>(total_kv)), dim3(256), 0, s, qq, kk,
+                     vv, e, emin, emax, lse, di, gg, static_cast<bf16_t*>(dk),
+                     static_cast<bf16_t*>(dv), B, N, Hq, Hkv, ntiles, nkt,
+                     static_cast<int>(total_kv), scale);
+  st = ks_check_launch("ks_evict_attn_bwd(dkdv)");
+  if (st != KS_OK) return st;
+
+  const int rs = 4 / hpw;
+  const int nqt = (N + 64 * rs - 1) / (64 * rs);
+  const long long real_q = static_cast<long long>(B) * (Hq / hpw) * nqt;
+  const long long total_q = (real_q + 7) / 8 * 8;
+  KS_REQUIRE(total_q < (1LL << 31), "ks_evict_attn_bwd: grid too large");
+#define KS_DQ_LAUNCH(HPW_)                                                                     \
+  hipLaunchKernelGGL((dq_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(256), 0, s,  \
+                     qq, kk, vv, e, emin, emax, lse, di, gg, static_cast<bf16_t*>(dq), B, N, Hq, \
+                     Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
+  if (hpw == 4) KS_DQ_LAUNCH(4);
+  else if (hpw == 2) KS_DQ_LAUNCH(2);
+  else KS_DQ_LAUNCH(1);
+#undef KS_DQ_LAUNCH
+  return ks_check_launch("ks_evict_attn_bwd(dq)");
+}

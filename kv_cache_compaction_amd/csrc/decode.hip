@@ -1,0 +1,283 @@
+// Paged GQA decode over compacted block tables.
+//
+// After compaction the block table lists only surviving 16-token blocks
+// (KV-streams explainer, block-table paragraph), and cached keys carry the
+// rotation of their logical positions (explainer, RoPE paragraph), so one
+// decode step is plain softmax attention of the new query over the tokens
+// reached through the table.
+//
+// Kernel 1 (split): one 64-lane wave per (sequence, group of HPW query heads
+// of one kv head, split of kSplit blocks).  Lane (t, g) = (lane % 16,
+// lane / 16) owns token slot t of every block and the 32 head-dim entries
+// d = 32s + 8g + i (s, i < 4, 8).  Per block each lane issues four 16-byte
+// loads of K and four of V at those entries, so every load instruction covers
+// 64 contiguous bytes of each of the block's 16 token rows.
+//   * Q K^T runs on the 16x16x32 bf16 MFMA: A = Q (rows = heads, replicated),
+//     B = K^T (columns = the 16 tokens).  The result leaves S[h][t] in lane
+//     (t, any g), i.e. exactly where the PV step needs it.
+//   * P V is VALU work: lane (t, g) accumulates p[h][t] * v[t][d] for its
+//     32 entries and HPW heads (FMA count is fixed by the problem; this
+//     layout needs no cross-lane traffic in the loop).
+//   * Softmax is online per lane with a lazily updated maximum: the running
+//     max only moves when a score exceeds it by more than 2^kTau, so the
+//     accumulator is rescaled on a handful of blocks instead of every block.
+//   * At the end the 16 token slots are merged with DPP row rotations.
+// Kernel 2 (reduce): merges the splits of each (sequence, head).
+//
+// Memory: K and V of every live token are read exactly once per step; the
+// split partials add 4(D+2) bytes per (sequence, head, split).
+#include "ks_common.h"
+
+namespace {
+
+constexpr int D = 128;
+constexpr int kSplit = 32;     // blocks per split
+constexpr float kTau = 8.0f;   // lazy-rescale slack, log2 units
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// all-reduce over the 16 lanes of a DPP row
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0x128>(x);  // row_ror:8
+  x += dpp<0x124>(x);  // row_ror:4
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  return x;
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp<0x128>(x));
+  x = fmaxf(x, dpp<0x124>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0xB1>(x));
+  return x;
+}
+
+struct BlockRegs {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+template <int HPW>
+__global__ __launch_bounds__(64) void decode_split_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kpool,
+    const bf16_t* __restrict__ vpool, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int Hq, int Hkv, int MB, int NB, int nsplit_max,
+    float sl2) {
+  const int split = blockIdx.x, hw = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int hq0 = hw * HPW;
+  const int hkv = hq0 / G;
+  // lengths beyond the table's capacity are clamped: nothing past a table
+  // row is ever read
+  const int L = min(max(seq_lens[b], 0), 16 * MB);
+  const int nblk = (L + 15) >> 4;
+  const int blk0 = split * kSplit;
+  if (blk0 >= nblk) return;
+  const int blk1 = min(nblk, blk0 + kSplit);
+  const int lane = threadIdx.x;
+  const int t = lane & 15, g = lane >> 4;
+
+  bf16x8 qa[4];
+  {
+    const bf16_t* qrow = q + (static_cast<size_t>(b) * Hq + hq0 + (t % HPW)) * D + g * 8;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 32);
+  }
+  float m[HPW], l[HPW], acc[HPW][32];
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    m[h] = -1e30f;
+    l[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[h][i] = 0.f;
+  }
+  const int32_t* trow = table + static_cast<size_t>(b) * MB;
+  bool bad = false;
+
+  auto load = [&](int blk, BlockRegs& r) {
+    const int pid = trow[blk];
+    const bool ok = static_cast<unsigned>(pid) < static_cast<unsigned>(NB);
+    bad |= !ok;
+    const size_t off =
+        ((static_cast<size_t>(ok ? pid : 0) * Hkv + hkv) * 16 + t) * D + g * 8;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      r.k[s] = *reinterpret_cast<const u32x4*>(kpool + off + s * 32);
+      r.v[s] = *reinterpret_cast<const u32x4*>(vpool + off + s * 32);
+    }
+  };
+
+  auto compute = [&](int blk, BlockRegs& r) {
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      sacc = mfma16x16x32(qa[s], __builtin_bit_cast(bf16x8, r.k[s]), sacc);
+    const bool valid = blk * 16 + t < L;
+    if ((blk + 1) * 16 > L) {  // tail block: slots past L may hold anything
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[s][i] = valid ? r.v[s][i] : 0u;
+    }
+    float sc[HPW];
+    bool need_any = false;
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      sc[h] = valid ? sacc[h] * sl2 : -INFINITY;
+      need_any |= sc[h] > m[h] + kTau;
+    }
+    if (__ballot(need_any)) {
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        const bool need = sc[h] > m[h] + kTau;
+        const float f = need ? fast_exp2(m[h] - sc[h]) : 1.f;
+        m[h] = need ? sc[h] : m[h];
+        l[h] *= f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[h][i] *= f;
+      }
+    }
+    float vf[32];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vf[s * 8 + 2 * i] = lo_bf16(r.v[s][i]);
+        vf[s * 8 + 2 * i + 1] = hi_bf16(r.v[s][i]);
+      }
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      const float p = fast_exp2(sc[h] - m[h]);
+      l[h] += p;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[h][i] = fmaf(p, vf[i], acc[h][i]);
+    }
+  };
+
+  BlockRegs r0, r1;
+  load(blk0, r0);
+  int blk = blk0;
+  for (; blk + 1 < blk1; blk += 2) {
+    load(blk + 1, r1);
+    compute(blk, r0);
+    if (blk + 2 < blk1) load(blk + 2, r0);
+    compute(blk + 1, r1);
+  }
+  if (blk < blk1) compute(blk, r0);
+
+  // merge the 16 token slots of each lane row (lanes with equal g)
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    const float M = row_max16(m[h]);
+    const float f = fast_exp2(m[h] - M);
+    float lsum = row_sum16(l[h] * f);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[h][i] = row_sum16(acc[h][i] * f);
+    if (bad) lsum = NAN;
+    if (t == 0) {
+      const size_t slot = (static_cast<size_t>(b) * Hq + hq0 + h) * nsplit_max + split;
+      float* po = part_o + slot * D + g * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f32x4* p4 = reinterpret_cast<f32x4*>(po + s * 32);
+        p4[0] = f32x4{acc[h][s * 8 + 0], acc[h][s * 8 + 1], acc[h][s * 8 + 2], acc[h][s * 8 + 3]};
+        p4[1] = f32x4{acc[h][s * 8 + 4], acc[h][s * 8 + 5], acc[h][s * 8 + 6], acc[h][s * 8 + 7]};
+      }
+      if (g == 0) {
+        part_ml[slot * 2 + 0] = M;
+        part_ml[slot * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(D) void decode_reduce_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ seq_lens, bf16_t* __restrict__ out, float* __restrict__ lse,
+    int Hq, int MB, int nsplit_max) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int L = min(max(seq_lens[b], 0), 16 * MB);
+  const int ns = (((L + 15) >> 4) + kSplit - 1) / kSplit;
+  const size_t slot0 = (static_cast<size_t>(b) * Hq + h) * nsplit_max;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(slot0 + s) * 2]);
+  float den = 0.f, num = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float f = fast_exp2(part_ml[(slot0 + s) * 2] - M);
+    den += part_ml[(slot0 + s) * 2 + 1] * f;
+    num += part_o[(slot0 + s) * D + d] * f;
+  }
+  const size_t o = (static_cast<size_t>(b) * Hq + h) * D + d;
+  if (ns == 0) {
+    out[o] = 0;
+    if (lse && d == 0) lse[static_cast<size_t>(b) * Hq + h] = -INFINITY;
+    return;
+  }
+  out[o] = f32_to_bf16(num / den);
+  if (lse && d == 0) lse[static_cast<size_t>(b) * Hq + h] = (M + __log2f(den)) * KS_LN2;
+}
+
+inline int nsplit_for(int max_blocks) { return (max_blocks + kSplit - 1) / kSplit; }
+
+}  // namespace
+
+extern "C" size_t ks_paged_decode_workspace(int B, int Hq, int Dh, int max_blocks) {
+  if (B <= 0 || Hq <= 0 || Dh <= 0 || max_blocks <= 0) return 0;
+  const size_t slots = static_cast<size_t>(B) * Hq * nsplit_for(max_blocks);
+  return slots * (static_cast<size_t>(Dh) + 2) * sizeof(float) + 256;
+}
+
+extern "C" ks_status ks_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* table, const int32_t* seq_lens, void* out,
+                                     float* lse, int B, int Hq, int Hkv, int Dh, int max_blocks,
+                                     int num_pool_blocks, int dtype, float scale, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  KS_REQUIRE(B >= 0 && Hq > 0 && Hkv > 0 && max_blocks >= 0 && num_pool_blocks >= 0,
+             "ks_paged_decode: bad sizes");
+  KS_REQUIRE(Hq % Hkv == 0, "ks_paged_decode: Hq %% Hkv != 0");
+  if (dtype != KS_BF16 || Dh != D)
+    return ks_fail(KS_ERR_UNSUPPORTED, "ks_paged_decode: only bf16 with D=128 (got dtype=%d D=%d)",
+                   dtype, Dh);
+  const int G = Hq / Hkv;
+  const int hpw = G >= 4 ? 4 : G;
+  if (G % hpw != 0)
+    return ks_fail(KS_ERR_UNSUPPORTED, "ks_paged_decode: group size %d unsupported", G);
+  if (B == 0) return KS_OK;
+  KS_REQUIRE(q && k_pool && v_pool && table && seq_lens && out, "ks_paged_decode: null pointer");
+  KS_REQUIRE(ks_aligned16(q) && ks_aligned16(k_pool) && ks_aligned16(v_pool) && ks_aligned16(out),
+             "ks_paged_decode: tensors must be 16-byte aligned");
+  // max_blocks == 0: every length clamps to 0 and no table entry is read
+  const size_t need = ks_paged_decode_workspace(B, Hq, Dh, max_blocks > 0 ? max_blocks : 1);
+  if (!ws || ws_bytes < need)
+    return ks_fail(KS_ERR_WORKSPACE, "ks_paged_decode: workspace %zu < %zu bytes", ws_bytes, need);
+  const int nsplit = max_blocks > 0 ? nsplit_for(max_blocks) : 1;
+  KS_REQUIRE(nsplit < 65536 && B < 65536, "ks_paged_decode: grid too large");
+  float* part_ml = static_cast<float*>(ws);
+  const size_t slots = static_cast<size_t>(B) * Hq * nsplit;
+  float* part_o = reinterpret_cast<float*>(
+      (reinterpret_cast<uintptr_t>(part_ml + 2 * slots) + 255) & ~static_cast<uintptr_t>(255));
+  const float sl2 = scale * KS_LOG2E;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(nsplit, Hq / hpw, B);
+  const bf16_t* qq = static_cast<const bf16_t*>(q);
+  const bf16_t* kp = static_cast<const bf16_t*>(k_pool);
+  const bf16_t* vp = static_cast<const bf16_t*>(v_pool);
+  if (hpw == 4)
+    hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(64), 0, s, qq, kp, vp, table, seq_lens,
+                       part_o, part_ml, Hq, Hkv, max_blocks, num_pool_blocks, nsplit, sl2);
+  else if (hpw == 2)
+    hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(64), 0, s, qq, kp, vp, table, seq_lens,
+                       part_o, part_ml, Hq, Hkv, max_blocks, num_pool_blocks, nsplit, sl2);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(64), 0, s, qq, kp, vp, table, seq_lens,
+                       part_o, part_ml, Hq, Hkv, max_blocks, num_pool_blocks, nsplit, sl2);
+  ks_status st = ks_check_launch("ks_paged_decode(split)");
+  if (st != KS_OK) return st;
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3(Hq, B), dim3(D), 0, s, part_o, part_ml, seq_lens,
+                     static_cast<bf16_t*>(out), lse, Hq, max_blocks, nsplit);
+  return ks_check_launch("ks_paged_decode(reduce)");
+}

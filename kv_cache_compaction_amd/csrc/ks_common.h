@@ -1,0 +1,70 @@
+// Internal helpers shared by the libks kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ks.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t bf16_t;  // storage type of one bf16 value
+
+// ---------------------------------------------------------------------------
+// host-side error plumbing (defined in ks_api.cpp)
+// ---------------------------------------------------------------------------
+ks_status ks_fail(ks_status st, const char* fmt, ...);
+ks_status ks_check_launch(const char* what);
+
+#define KS_REQUIRE(cond, ...)                                  \
+  do {                                                         \
+    if (!(cond)) return ks_fail(KS_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+static inline bool ks_aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (the gfx950 conversion instruction)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+// two fp32 -> packed bf16 pair (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// lane index within the 64-wide wavefront
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+static constexpr float KS_LOG2E = 1.4426950408889634f;
+static constexpr float KS_LN2 = 0.6931471805599453f;

@@ -1,0 +1,143 @@
+"""GPU parity of compaction + paged GQA decode against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compaction_amd as ks
+import oracle as O
+from parity_util import announce, f64, gate
+from workloads import CONFIGS, build_decode_batch, normal_tensor
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    announce(request.node.nodeid)
+
+
+def _gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def run_decode_case(db, Hq, Hkv, D=128, seed=0, poison=True, base=10000.0):
+    """Compaction rounds + RoPE(q at T) + paged decode on the GPU; the oracle
+    does the same from the same inputs.  Returns (got_out, got_lse, ref_out,
+    ref_lse)."""
+    B, MB = db.table0.shape
+    NB = db.num_pool_blocks
+    kp = normal_tensor((NB, Hkv, 16, D), seed + 1, 0.5, torch.bfloat16, DEV)
+    vp = normal_tensor((NB, Hkv, 16, D), seed + 2, 0.5, torch.bfloat16, DEV)
+    q_raw = normal_tensor((B, Hq, D), seed + 3, 0.5, torch.bfloat16, "cpu")
+    if poison:
+        # evicted blocks and the unused slots of the decode block hold NaN
+        dead = []
+        for b in range(B):
+            for (x0, x1) in db.runs[b]:
+                dead.extend(int(p) for p in db.table0[b, x0:x1])
+        if dead:
+            idx = torch.tensor(dead, dtype=torch.long, device=DEV)
+            kp[idx] = float("nan")
+            vp[idx] = float("nan")
+        fresh = torch.tensor([int(db.table0[b, db.nblk0[b] - 1]) for b in range(B)],
+                             dtype=torch.long, device=DEV)
+        kp[fresh, :, 1:] = float("nan")
+        vp[fresh, :, 1:] = float("nan")
+    # compaction rounds, ping-pong
+    ta, tb = _gpu(db.table0), torch.empty((B, MB), dtype=torch.int32, device=DEV)
+    na, nb = _gpu(db.nblk0), torch.empty(B, dtype=torch.int32, device=DEV)
+    for r in range(db.keeps.shape[0]):
+        ks.ks_compact_block_table(ta, na, _gpu(db.keeps[r]), tb, nb)
+        ta, tb, na, nb = tb, ta, nb, na
+    seq_lens = _gpu((db.live_len + 1).astype(np.int32))
+    q = q_raw.to(DEV)[:, None]                               # [B, 1, Hq, D]
+    ks.ks_rope_logical(q, None, _gpu(db.pos[:, None].astype(np.int32)), base=base)
+    out, lse = ks.ks_paged_decode(q[:, 0].contiguous(), kp, vp, ta, seq_lens)
+    torch.cuda.synchronize()
+
+    # oracle: its own compaction, its own rotation, the same pool contents
+    rt, rn = db.table0, db.nblk0
+    for r in range(db.keeps.shape[0]):
+        rt, rn = O.compact_block_table(rt, rn, db.keeps[r])
+    np.testing.assert_array_equal(ta.cpu().numpy(), rt)      # bit-exact tables
+    np.testing.assert_array_equal(na.cpu().numpy(), rn)
+    L = db.live_len + 1
+    need = [rt[b, :(int(L[b]) + 15) // 16] for b in range(B)]
+    ids = np.unique(np.concatenate(need))
+    remap = {int(p): i for i, p in enumerate(ids)}
+    idx = torch.from_numpy(ids.astype(np.int64)).to(DEV)
+    kh = kp.index_select(0, idx).float().cpu().numpy()
+    vh = vp.index_select(0, idx).float().cpu().numpy()
+    rt2 = np.full_like(rt, -1)
+    for b in range(B):
+        rt2[b, :len(need[b])] = [remap[int(p)] for p in need[b]]
+    qr = O.rope(f64(q_raw)[:, None], db.pos[:, None], base)[:, 0]
+    ro, rl = O.paged_decode(qr, kh, vh, rt2, L)
+    return out, lse, ro, rl
+
+
+def test_cfg4_full_compaction_then_decode():
+    cfg = CONFIGS[4]
+    db = build_decode_batch(np.random.default_rng(1000 + 4), cfg.batch)
+    out, lse, ro, rl = run_decode_case(db, cfg.Hq, cfg.Hkv, seed=4000)
+    gate(out, ro, "bf16", "decode out")
+    gate(lse, rl, "bf16", "decode lse")
+
+
+@pytest.mark.parametrize("Hq,Hkv,seed", [(32, 8, 1), (64, 8, 2), (8, 4, 3), (4, 4, 4)])
+def test_small_batches_group_sizes(Hq, Hkv, seed):
+    db = build_decode_batch(np.random.default_rng(seed), 5, live_range=(160, 1200),
+                            max_pos=4096)
+    out, lse, ro, rl = run_decode_case(db, Hq, Hkv, seed=seed * 10)
+    gate(out, ro, "bf16", "decode out")
+    gate(lse, rl, "bf16", "decode lse")
+
+
+def _direct(B, Hq, Hkv, lens, seed, NB=None):
+    """Simple pool + table, no compaction: table_b = a permutation slice."""
+    D = 128
+    nbs = [(int(x) + 15) // 16 for x in lens]
+    MB = max(max(nbs), 1)
+    NB = NB or max(sum(nbs), 1)
+    perm = np.random.default_rng(seed).permutation(NB).astype(np.int32)
+    table = np.full((B, MB), -1, np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nbs[b]] = perm[off:off + nbs[b]]
+        off += nbs[b]
+    kp = normal_tensor((NB, Hkv, 16, D), seed + 1, 0.5, torch.bfloat16, DEV)
+    vp = normal_tensor((NB, Hkv, 16, D), seed + 2, 0.5, torch.bfloat16, DEV)
+    q = normal_tensor((B, Hq, D), seed + 3, 0.5, torch.bfloat16, DEV)
+    return q, kp, vp, table
+
+
+def test_ragged_tails_zero_and_one_token():
+    lens = np.array([0, 1, 15, 16, 17, 513, 1000], np.int32)
+    B, Hq, Hkv = len(lens), 8, 2
+    q, kp, vp, table = _direct(B, Hq, Hkv, lens, 77)
+    # poison everything past each sequence's length
+    for b in range(B):
+        n = int(lens[b])
+        if n % 16:
+            kp[int(table[b, n // 16]), :, n % 16:] = float("nan")
+            vp[int(table[b, n // 16]), :, n % 16:] = float("nan")
+    out, lse = ks.ks_paged_decode(q, kp, vp, _gpu(table), _gpu(lens))
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and math.isinf(lse[0, 0].item()) and lse[0, 0].item() < 0
+    ro, rl = O.paged_decode(f64(q[1:]), kp.float().cpu().numpy(), vp.float().cpu().numpy(),
+                            table[1:], lens[1:])
+    gate(out[1:], ro, "bf16", "decode out")
+    gate(lse[1:], rl, "bf16", "decode lse")
+
+
+def test_invalid_block_id_gives_nan_not_fault():
+    lens = np.array([40, 40], np.int32)
+    q, kp, vp, table = _direct(2, 4, 1, lens, 88)
+    table[1, 1] = kp.shape[0] + 5          # out of range
+    out, _ = ks.ks_paged_decode(q, kp, vp, _gpu(table), _gpu(lens))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[0].float()).all()
+    assert torch.isnan(out[1].float()).all()

@@ -1,0 +1,96 @@
+"""Host-side checks of libks.so that need no GPU: the library loads, exports
+every function include/ks.h declares, and rejects bad arguments before it
+launches anything."""
+import ctypes
+import subprocess
+
+import pytest
+
+import kv_cache_compaction_amd as ks
+from kv_cache_compaction_amd import _lib
+
+FAKE = ctypes.c_void_p(4096)  # aligned non-null; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ks.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = ks.header_functions()
+    assert {"ks_rope_logical", "ks_evict_attn_fwd", "ks_evict_attn_bwd",
+            "ks_compact_block_table", "ks_paged_decode", "ks_last_error"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", ks.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(lib, n)
+    assert lib.ks_version().startswith(b"libks")
+
+
+def _status(lib, fn, *args):
+    st = getattr(lib, fn)(*args)
+    return st, lib.ks_last_error().decode()
+
+
+def test_compaction_rejects_aliasing(lib):
+    st, msg = _status(lib, "ks_compact_block_table", FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                      4, 32, None)
+    assert st == 1 and "alias" in msg
+    st, msg = _status(lib, "ks_compact_block_table", FAKE, FAKE, FAKE, ctypes.c_void_p(1 << 20),
+                      FAKE, FAKE, None, 4, 32, None)
+    assert st == 1 and "pos_in" in msg
+    st, _ = _status(lib, "ks_compact_block_table", None, None, None, None, None, None, None, 0,
+                    32, None)
+    assert st == 0  # B == 0 is a no-op
+
+
+def test_attention_argument_checks(lib):
+    # Hq not a multiple of Hkv
+    st, msg = _status(lib, "ks_evict_attn_fwd", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 3, 2,
+                      128, 1, 0.1, FAKE, 1 << 20, None)
+    assert st == 1 and "Hq" in msg
+    # unsupported head dim for bf16
+    st, _ = _status(lib, "ks_evict_attn_fwd", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 4, 2, 96,
+                    1, 0.1, FAKE, 1 << 20, None)
+    assert st == 2
+    # workspace too small
+    need = lib.ks_evict_attn_fwd_workspace(1, 4096, 8, 2, 128, 1)
+    assert need > 0
+    st, msg = _status(lib, "ks_evict_attn_fwd", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 8,
+                      2, 128, 1, 0.1, FAKE, need - 1, None)
+    assert st == 4 and "workspace" in msg
+    # misaligned tensor
+    st, msg = _status(lib, "ks_evict_attn_fwd", ctypes.c_void_p(4098), FAKE, FAKE, FAKE, FAKE,
+                      FAKE, 1, 64, 4, 2, 128, 1, 0.1, FAKE, 1 << 20, None)
+    assert st == 1 and "aligned" in msg
+    # backward: fp32 is not provided
+    st, _ = _status(lib, "ks_evict_attn_bwd", *([FAKE] * 10), 1, 64, 4, 2, 128, 0, 0.1, FAKE,
+                    1 << 20, None)
+    assert st == 2
+    need_b = lib.ks_evict_attn_bwd_workspace(2, 1000, 8, 2, 128, 1)
+    assert need_b >= 2 * 1000 * 8 * 4
+
+
+def test_decode_and_rope_argument_checks(lib):
+    st, _ = _status(lib, "ks_paged_decode", *([FAKE] * 7), 2, 32, 8, 64, 10, 100, 1, 0.1, FAKE,
+                    1 << 20, None)
+    assert st == 2  # D = 64 not provided for decode
+    need = lib.ks_paged_decode_workspace(64, 32, 128, 4097)
+    st, msg = _status(lib, "ks_paged_decode", *([FAKE] * 7), 64, 32, 8, 128, 4097, 10, 1, 0.1,
+                      FAKE, need - 1, None)
+    assert st == 4
+    st, _ = _status(lib, "ks_rope_logical", FAKE, FAKE, FAKE, 1, 8, 4, 2, 100, 1, 10000.0, 0,
+                    None)
+    assert st == 1  # D must be a multiple of 16
+    st, _ = _status(lib, "ks_rope_logical", FAKE, FAKE, FAKE, 1, 8, 4, 2, 64, 7, 10000.0, 0,
+                    None)
+    assert st == 1  # bad dtype
+
+
+def test_python_binding_error_type():
+    err = _lib.KSError("ks_x", 4, "workspace 1 < 2 bytes")
+    assert "WORKSPACE_TOO_SMALL" in str(err) and err.status == 4
