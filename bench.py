@@ -1,0 +1,316 @@
+"""Benchmark of the KV-streams hot path on one MI355X.
+
+One step = one pass of every hot-path stage over one batch of synthetic input:
+  training side (4 x 32k-token summary-compaction traces, 32 q / 8 kv heads,
+  D = 128, bf16): RoPE at logical positions on Q and K, eviction-masked
+  attention forward, then backward;
+  inference side (64 paged caches, 32 q / 8 kv heads): 1-6 rounds of
+  block-table compaction, RoPE of the decode query at its logical position,
+  one paged GQA decode step.
+
+Prints one JSON line.  `value` is the masked attention fwd+bwd throughput in
+TFLOP/s of useful work (4*D flops forward and 10*D backward per live
+(query, key) pair per query head; masked pairs are not counted), timed with
+HIP events on the stream the kernels run on.  The decode side's HBM GB/s is
+reported beside it.  `cpu_baseline` times the fp64 oracle on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def live_pairs(e: np.ndarray) -> int:
+    """sum over queries of |{j <= i : e_j > i}| for a batch of traces."""
+    tot = 0
+    for row in e.astype(np.int64):
+        N = row.size
+        hist = np.zeros(N + 1, dtype=np.int64)
+        np.add.at(hist, row[row < N], 1)
+        gone = np.cumsum(hist)[:N]
+        tot += int(((np.arange(N) + 1) - gone).sum())
+    return tot
+
+
+class Timer:
+    """HIP-event timing of one stage on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        return ev
+
+    def stop(self, ev0, name):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.pairs.append((name, ev0, ev))
+
+    def totals(self):
+        out = {}
+        for name, a, b in self.pairs:
+            out[name] = out.get(name, 0.0) + a.elapsed_time(b)
+        return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by (trace, kv group) and by sequence without exchange, see "
+              "DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import kv_cache_compaction_amd as ks
+    from workloads import CONFIGS, build_decode_batch, config_trace_batch, normal_tensor, \
+        stacked_e
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    bf = torch.bfloat16
+
+    # ---------------- training-side inputs (32k summary traces) ----------------
+    c3 = CONFIGS[3]
+    traces, seeds = config_trace_batch(c3)
+    e_np = stacked_e(traces)
+    B, N, Hq, Hkv, D = c3.batch, c3.N, c3.Hq, c3.Hkv, c3.D
+    q = normal_tensor((B, N, Hq, D), seeds["q"], c3.value_scale, bf, dev)
+    k = normal_tensor((B, N, Hkv, D), seeds["k"], c3.value_scale, bf, dev)
+    v = normal_tensor((B, N, Hkv, D), seeds["v"], c3.value_scale, bf, dev)
+    do = normal_tensor((B, N, Hq, D), seeds["do"], c3.value_scale, bf, dev)
+    e = torch.from_numpy(e_np).to(dev)
+    pos = torch.arange(N, dtype=torch.int32, device=dev)[None].repeat(B, 1).contiguous()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_f = torch.empty(ks.ks_evict_attn_fwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(ks.ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+                       dtype=torch.uint8, device=dev)
+    pairs = live_pairs(e_np)
+    # live pairs summed over the traces; every query head sees its trace's mask
+    flops_fwd = 4.0 * D * pairs * Hq
+    flops_bwd = 10.0 * D * pairs * Hq
+    causal_pairs = B * N * (N + 1) // 2
+
+    # ---------------- inference-side inputs (paged decode) ----------------
+    c4 = CONFIGS[4]
+    db = build_decode_batch(np.random.default_rng(1000 + 4), c4.batch)
+    DB, MB = db.table0.shape
+    NB = db.num_pool_blocks
+    H4q, H4kv = c4.Hq, c4.Hkv
+    kp = normal_tensor((NB, H4kv, 16, D), 4001, 0.5, bf, dev)
+    vp = normal_tensor((NB, H4kv, 16, D), 4002, 0.5, bf, dev)
+    q4 = normal_tensor((DB, 1, H4q, D), 4003, 0.5, bf, dev)
+    pos4 = torch.from_numpy(db.pos[:, None].astype(np.int32)).to(dev)
+    table0 = torch.from_numpy(db.table0).to(dev)
+    nblk0 = torch.from_numpy(db.nblk0).to(dev)
+    keeps = [torch.from_numpy(db.keeps[r]).to(dev) for r in range(db.keeps.shape[0])]
+    tbufs = [torch.empty_like(table0), torch.empty_like(table0)]
+    nbufs = [torch.empty_like(nblk0), torch.empty_like(nblk0)]
+    seq_lens = torch.from_numpy((db.live_len + 1).astype(np.int32)).to(dev)
+    out4 = torch.empty((DB, H4q, D), dtype=bf, device=dev)
+    lse4 = torch.empty((DB, H4q), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(ks.ks_paged_decode_workspace(DB, H4q, D, MB), dtype=torch.uint8,
+                       device=dev)
+    L = db.live_len.astype(np.int64) + 1
+    dec_bytes = int((L * H4kv * D * 2 * 2).sum()) + 2 * DB * H4q * D * 2 + \
+        int(((L + 15) // 16).sum()) * 4 + DB * 4 + DB * H4q * 4
+    comp_bytes = 0
+    nb_cur = db.nblk0.astype(np.int64).copy()
+    for r in range(db.keeps.shape[0]):
+        comp_bytes += int(nb_cur.sum()) * 5 + DB * MB * 4 + DB * 8
+        nb_cur = np.array([int(db.keeps[r, b, :nb_cur[b]].sum()) for b in range(DB)])
+    R = len(keeps)
+
+    stream = torch.cuda.current_stream()
+
+    def step(tm=None):
+        def t0():
+            return tm.start() if tm else None
+
+        def t1(ev, name):
+            if tm:
+                tm.stop(ev, name)
+        ev = t0()
+        ks.ks_rope_logical(q, k, pos, stream=stream)
+        t1(ev, "rope")
+        ev = t0()
+        ks.ks_evict_attn_fwd(q, k, v, e, out=o, lse=lse, ws=ws_f, stream=stream)
+        t1(ev, "attn_fwd")
+        ev = t0()
+        ks.ks_evict_attn_bwd(q, k, v, e, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws_b, stream=stream)
+        t1(ev, "attn_bwd")
+        ev = t0()
+        src, srcn = table0, nblk0
+        for r in range(R):
+            ks.ks_compact_block_table(src, srcn, keeps[r], tbufs[r % 2], nbufs[r % 2],
+                                      stream=stream)
+            src, srcn = tbufs[r % 2], nbufs[r % 2]
+        t1(ev, "compact")
+        ev = t0()
+        ks.ks_rope_logical(q4, None, pos4, stream=stream)
+        ks.ks_paged_decode(q4[:, 0], kp, vp, src, seq_lens, out=out4, lse=lse4, ws=ws_d,
+                           stream=stream)
+        t1(ev, "decode")
+
+    # q4[:, 0] is a view of a contiguous [B, 1, Hq, D] tensor: contiguous as [B, Hq, D]
+    assert q4[:, 0].is_contiguous()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(tm)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    tot = tm.totals()
+    K = args.steps
+    ms = {kk: vv / K for kk, vv in tot.items()}
+    attn_ms = ms["attn_fwd"] + ms["attn_bwd"]
+    tflops = (flops_fwd + flops_bwd) / (attn_ms * 1e-3) / 1e12
+    dec_gbs = (dec_bytes + comp_bytes) / ((ms["decode"] + ms["compact"]) * 1e-3) / 1e9
+    parts = {
+        "attn_fwd": {"bound": "mfma", "ms": ms["attn_fwd"],
+                     "achieved": flops_fwd / (ms["attn_fwd"] * 1e-3) / 1e12,
+                     "unit": "TFLOP/s"},
+        "attn_bwd": {"bound": "mfma", "ms": ms["attn_bwd"],
+                     "achieved": flops_bwd / (ms["attn_bwd"] * 1e-3) / 1e12,
+                     "unit": "TFLOP/s"},
+        "decode": {"bound": "hbm", "ms": ms["decode"],
+                   "achieved": dec_bytes / (ms["decode"] * 1e-3) / 1e9, "unit": "GB/s"},
+        "compact": {"bound": "hbm", "ms": ms["compact"],
+                    "achieved": comp_bytes / (ms["compact"] * 1e-3) / 1e9, "unit": "GB/s"},
+        "rope": {"bound": "hbm", "ms": ms["rope"],
+                 "achieved": 2 * (q.numel() + k.numel()) * 2 / (ms["rope"] * 1e-3) / 1e9,
+                 "unit": "GB/s"},
+    }
+    for p in parts.values():
+        peak = MFMA_BF16_PEAK_TFLOPS if p["bound"] == "mfma" else HBM_PEAK_GBS
+        p["frac"] = p["achieved"] / peak
+    dom = max(("attn_fwd", "attn_bwd"), key=lambda x: ms[x])
+    result = {
+        "metric": "eviction-masked attn fwd+bwd TFLOP/s @32k trace; paged-decode HBM GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded traces and N(0,1)*0.5 tensors; no dataset or weights)",
+        "config": {
+            "workload": "4 x 32768-token summary-compaction traces (P=512, B=8192, o=1024, "
+                        "s=512), 32 q / 8 kv heads, D=128, fwd+bwd; plus paged decode of 64 "
+                        "compacted caches (4k-16k live tokens, 1-6 events), 32 q / 8 kv heads",
+            "global_batch": B, "seq_len": N, "parallelism": "single GPU",
+            "live_pairs_per_head": pairs, "causal_fraction": round(pairs / causal_pairs, 4),
+        },
+        "decode_hbm_gbs": round(dec_gbs, 1),
+        "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "stage_ms": {kk: round(vv, 4) for kk, vv in ms.items()},
+        "roofline": {
+            "kernel": f"ks_{'evict_attn_bwd' if dom == 'attn_bwd' else 'evict_attn_fwd'}",
+            "bound": "mfma",
+            "achieved": round(parts[dom]["achieved"], 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(parts[dom]["frac"], 4),
+            "traffic": None,
+        },
+        "stages": {kk: {x: (round(y, 4) if isinstance(y, float) else y) for x, y in vv.items()}
+                   for kk, vv in parts.items()},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(traces, seeds, c3, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(traces, seeds, cfg, budget_s):
+    """Time the fp64 oracle (forward + backward on a prefix of one trace, one
+    query head at a time, until about budget_s seconds have passed) on the
+    host; report useful TFLOP/s with the GPU figure's flop convention."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    from workloads import normal_tensor
+
+    N, D, Hq, Hkv = cfg.N, cfg.D, cfg.Hq, cfg.Hkv
+    G = Hq // Hkv
+    tr = traces[0]
+    e = tr.e[None].astype(np.int64)
+    # raw projections of trace 0, kv head 0 (the generator draws whole tensors)
+    bf = torch.bfloat16
+    qh = normal_tensor((1, N, Hq, D), seeds["q"], cfg.value_scale, bf, "cuda")[:, :, :G]
+    kh = normal_tensor((1, N, Hkv, D), seeds["k"], cfg.value_scale, bf, "cuda")[:, :, :1]
+    vh = normal_tensor((1, N, Hkv, D), seeds["v"], cfg.value_scale, bf, "cuda")[:, :, :1]
+    dh = normal_tensor((1, N, Hq, D), seeds["do"], cfg.value_scale, bf, "cuda")[:, :, :G]
+    f = lambda t: t.to("cpu", torch.float64).numpy()
+    q, k, v, do = f(qh), f(kh), f(vh), f(dh)
+    pos = np.arange(N)[None]
+    q, k = O.rope(q, pos), O.rope(k, pos)
+    # prefix of the trace: rows < n only see keys < n, so the prefix is a
+    # complete masked-attention problem of its own
+    n = min(N, 16384)
+    en = e[:, :n]
+    pairs_n = int(O.eviction_mask(en[0], np.arange(n), n).sum())
+    done_pairs = 0
+    heads_used = 0
+    t0 = time.perf_counter()
+    while heads_used < G and (heads_used == 0 or time.perf_counter() - t0 < budget_s):
+        h = heads_used
+        qh1, doh1 = q[:, :n, h:h + 1], do[:, :n, h:h + 1]
+        O.attn_fwd(qh1, k[:, :n], v[:, :n], en)
+        O.attn_bwd(qh1, k[:, :n], v[:, :n], en, doh1)
+        done_pairs += pairs_n
+        heads_used += 1
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": round(14.0 * D * done_pairs / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 oracle forward + backward (dQ, dK, dV) of the first {n} tokens "
+                  f"of trace 0, {heads_used} query head(s) of kv group 0: {done_pairs} live "
+                  f"pairs in {el:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()
