@@ -488,6 +488,365 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV (8 waves, natural tiles): a workgroup owns 256 keys of one kv head,
+// 32 per wave.  K stays in registers as the B operand of S = Q K^T; V of the
+// 256 keys stays in LDS for the whole walk (B operand of dP = dO V^T).  Query
+// chunks of 32 rows are staged once, in natural layout; the transposed
+// operands of dV^T += dO^T P and dK^T += Q^T dS come from transpose reads.
+// Workgroups are ordered key-tile major so the heavy prompt tiles (whose
+// queries run to the end of the trace) start first.
+// ---------------------------------------------------------------------------
+constexpr int KW8 = 256;
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_d128_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
+    const int32_t* __restrict__ emax, const float* __restrict__ lse,
+    const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk,
+    bf16_t* __restrict__ dv, int B, int N, int Hq, int Hkv, int ntiles, float scale) {
+  __shared__ __attribute__((aligned(16))) bf16_t Vst[KW8 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Os[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+
+  const int nbh = B * Hkv;
+  const int kt = blockIdx.x / nbh;
+  const int bh = blockIdx.x % nbh;
+  const int b = bh / Hkv, hkv = bh % Hkv;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, lh = lane >> 5;
+  const int j0 = kt * KW8;
+  const int kw0 = j0 + 32 * w;
+  const int jl = kw0 + lq;
+  const size_t tokkv = static_cast<size_t>(Hkv) * D;
+  const size_t tokq = static_cast<size_t>(Hq) * D;
+  const float sl2 = scale * KS_LOG2E;
+
+  bf16x8 kf[NSTEP];
+  {
+    const size_t off = (static_cast<size_t>(b) * N + (jl < N ? jl : 0)) * tokkv +
+                       static_cast<size_t>(hkv) * D + lh * 8;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      u32x4 a = *reinterpret_cast<const u32x4*>(k + off + s * 16);
+      if (jl >= N) a = u32x4{0u, 0u, 0u, 0u};
+      kf[s] = __builtin_bit_cast(bf16x8, a);
+    }
+  }
+  const int ej = jl < N ? e[static_cast<size_t>(b) * N + jl] : 0;
+  // V of the workgroup's keys, staged once
+  for (int idx = tid; idx < KW8 * CH; idx += 512) {
+    const int row = idx >> 4, c = idx & 15;
+    const int j = j0 + row;
+    const u32x4 x = j < N ? *reinterpret_cast<const u32x4*>(
+                                v + (static_cast<size_t>(b) * N + j) * tokkv +
+                                static_cast<size_t>(hkv) * D + c * 8)
+                          : u32x4{0u, 0u, 0u, 0u};
+    tile_store_chunk(Vst, row, c, x);
+  }
+
+  const int t0 = j0 / kKeyTile;
+  const int t1 = min(ntiles - 1, t0 + KW8 / kKeyTile - 1);
+  int emx = static_cast<int>(0x80000000), emn = 0x7fffffff;
+  for (int t = t0; t <= t1; ++t) {
+    emx = max(emx, emax[static_cast<size_t>(b) * ntiles + t]);
+    emn = min(emn, emin[static_cast<size_t>(b) * ntiles + t]);
+  }
+  const int qend = min(N, emx);
+  int wemx = jl < N ? ej : static_cast<int>(0x80000000);
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) wemx = max(wemx, __shfl_xor(wemx, off));
+  const int wq1 = min(N, wemx);
+  const int kmax = min(N, j0 + KW8) - 1;
+
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dka[db][r] = dva[db][r] = 0.f;
+
+  const int c_begin = j0 / BQ;
+  const int c_end = (qend + BQ - 1) / BQ;
+  const int nc = c_end > c_begin ? c_end - c_begin : 0;
+  const int nchunks = nc * G;
+
+  // staging: thread t copies chunk (t & 15) of row (t >> 4) of Q and of dO
+  const int srow = tid >> 4, sc = tid & 15;
+  u32x4 xq, xo;
+  float lr = 0.f;
+  auto load_chunk = [&](int idx) {
+    const int h = hkv * G + idx / nc;
+    const int c0 = (c_begin + idx % nc) * BQ;
+    const int row = c0 + srow;
+    const size_t off = (static_cast<size_t>(b) * N + row) * tokq + static_cast<size_t>(h) * D +
+                       sc * 8;
+    const bool ok = row < N;
+    xq = ok ? *reinterpret_cast<const u32x4*>(q + off) : u32x4{0u, 0u, 0u, 0u};
+    xo = ok ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0u, 0u, 0u, 0u};
+    if (tid < 2 * BQ) {
+      const int r2 = c0 + (tid & (BQ - 1));
+      const size_t li = (static_cast<size_t>(b) * Hq + h) * N + r2;
+      if (tid < BQ)
+        lr = r2 < N ? lse[li] * KS_LOG2E : INFINITY;
+      else
+        lr = r2 < N ? di[li] : 0.f;
+    }
+  };
+  auto store_chunk = [&](int buf) {
+    tile_store_chunk(Qs[buf], srow, sc, xq);
+    tile_store_chunk(Os[buf], srow, sc, xo);
+    if (tid < BQ)
+      Ls[buf][tid] = lr;
+    else if (tid < 2 * BQ)
+      Ds[buf][tid - BQ] = lr;
+  };
+
+  auto compute = [&](int buf, int c0) {
+    if (c0 >= wq1 || c0 + BQ <= kw0) return;  // none of this wave's keys is seen
+    const bool full = (c0 >= kmax) && (c0 + BQ <= emn) && (c0 + BQ <= N);
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      sacc = mfma32x32x16(tile_chunk(Qs[buf], lq, 2 * s + lh), kf[s], sacc);
+      pacc = mfma32x32x16(tile_chunk(Os[buf], lq, 2 * s + lh),
+                          tile_chunk(Vst, 32 * w + lq, 2 * s + lh), pacc);
+    }
+    bf16x8 pf[2], sf[2];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int ql = rg * 8 + lh * 4;
+      const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][ql]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&Ds[buf][ql]);
+      const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = rg * 4 + c;
+        float p = fast_exp2(fmaf(sacc[r], sl2, -la[c]));
+        if (!full) {
+          const int i = c0 + ql + c;
+          const bool live = jl <= i && i < ej && i < N && jl < N;
+          p = live ? p : 0.f;
+        }
+        pf[r >> 3][r & 7] = (__bf16)p;
+        sf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - da[c]));
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dva[db] = mfma32x32x16(tile_frag_t(Os[buf], 16 * ks, 32 * db, lane), pf[ks], dva[db]);
+        dka[db] = mfma32x32x16(tile_frag_t(Qs[buf], 16 * ks, 32 * db, lane), sf[ks], dka[db]);
+      }
+  };
+
+  if (nchunks > 0) {
+    load_chunk(0);
+    store_chunk(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int idx = 0; idx < nchunks; ++idx) {
+    const bool more = idx + 1 < nchunks;
+    if (more) load_chunk(idx + 1);
+    compute(buf, (c_begin + idx % nc) * BQ);
+    if (more) store_chunk(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  if (jl < N) {
+    const size_t off = (static_cast<size_t>(b) * N + jl) * tokkv + static_cast<size_t>(hkv) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = db * 32 + rg * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(dk + off + d) =
+            u32x2{pack_bf16x2(dka[db][rg * 4] * scale, dka[db][rg * 4 + 1] * scale),
+                  pack_bf16x2(dka[db][rg * 4 + 2] * scale, dka[db][rg * 4 + 3] * scale)};
+        *reinterpret_cast<u32x2*>(dv + off + d) =
+            u32x2{pack_bf16x2(dva[db][rg * 4], dva[db][rg * 4 + 1]),
+                  pack_bf16x2(dva[db][rg * 4 + 2], dva[db][rg * 4 + 3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (8 waves, natural tiles): laid out like the forward, 32 query rows per
+// wave; K and V key tiles staged natural, K^T operands by transpose reads.
+// ---------------------------------------------------------------------------
+template <int HPW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_d128_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
+    const int32_t* __restrict__ emax, const float* __restrict__ lse,
+    const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
+    int B, int N, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale) {
+  constexpr int RS = 8 / HPW;
+  constexpr int BM = 32 * RS;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * D];
+  __shared__ __attribute__((aligned(16))) int Es[2][KT];
+
+  int lin = blockIdx.x;
+  lin = (lin & 7) * (total_wg >> 3) + (lin >> 3);
+  const int ngrp = Hq / HPW;
+  if (lin >= B * ngrp * nqt) return;
+  const int qt = lin % nqt;
+  const int grp = (lin / nqt) % ngrp;
+  const int b = lin / (nqt * ngrp);
+  const int G = Hq / Hkv;
+  const int hq0 = grp * HPW;
+  const int hkv = hq0 / G;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int hq = hq0 + (w % HPW);
+  const int i0 = qt * BM;
+  const int wi0 = i0 + (w / HPW) * 32;
+  const int i1 = min(N, i0 + BM);
+  const int lq = lane & 31, lh = lane >> 5;
+  const int qi = wi0 + lq;
+  const size_t tokkv = static_cast<size_t>(Hkv) * D;
+  const size_t tokq = static_cast<size_t>(Hq) * D;
+  const bf16_t* kb = k + static_cast<size_t>(b) * N * tokkv + static_cast<size_t>(hkv) * D;
+  const bf16_t* vb = v + static_cast<size_t>(b) * N * tokkv + static_cast<size_t>(hkv) * D;
+  const int32_t* eb = e + static_cast<size_t>(b) * N;
+  const int32_t* eminb = emin + static_cast<size_t>(b) * ntiles;
+  const float sl2 = scale * KS_LOG2E;
+
+  bf16x8 qf[NSTEP], gf[NSTEP];
+  float l2, dii;
+  {
+    const size_t off = (static_cast<size_t>(b) * N + (qi < N ? qi : 0)) * tokq +
+                       static_cast<size_t>(hq) * D + lh * 8;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      u32x4 a = *reinterpret_cast<const u32x4*>(q + off + s * 16);
+      u32x4 c = *reinterpret_cast<const u32x4*>(dout + off + s * 16);
+      if (qi >= N) a = c = u32x4{0u, 0u, 0u, 0u};
+      qf[s] = __builtin_bit_cast(bf16x8, a);
+      gf[s] = __builtin_bit_cast(bf16x8, c);
+    }
+    const size_t li = (static_cast<size_t>(b) * Hq + hq) * N + (qi < N ? qi : 0);
+    l2 = qi < N ? lse[li] * KS_LOG2E : INFINITY;
+    dii = qi < N ? di[li] : 0.f;
+  }
+  f32x16 dqa[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqa[db][r] = 0.f;
+
+  u32x4 kr[2], vr[2];
+  int er = 0;
+  auto load_tile = [&](int t) {
+    const int j0 = t * KT;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 512 * u;
+      const int j = j0 + (idx >> 4), c = idx & 15;
+      const bool ok = j < N;
+      kr[u] = ok ? *reinterpret_cast<const u32x4*>(kb + j * tokkv + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      vr[u] = ok ? *reinterpret_cast<const u32x4*>(vb + j * tokkv + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < KT) er = (j0 + tid < N) ? eb[j0 + tid] : 0;
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 512 * u;
+      tile_store_chunk(Ks[buf], idx >> 4, idx & 15, kr[u]);
+      tile_store_chunk(Vs[buf], idx >> 4, idx & 15, vr[u]);
+    }
+    if (tid < KT) Es[buf][tid] = er;
+  };
+
+  auto compute = [&](int buf, int j0, bool partial) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        sacc = mfma32x32x16(tile_chunk(Ks[buf], kk * 32 + lq, 2 * s + lh), qf[s], sacc);
+        pacc = mfma32x32x16(tile_chunk(Vs[buf], kk * 32 + lq, 2 * s + lh), gf[s], pacc);
+      }
+      bf16x8 sf[2];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int kl = kk * 32 + rg * 8 + lh * 4;
+        int ee[4] = {0, 0, 0, 0};
+        if (partial) {
+          const int4 ev = *reinterpret_cast<const int4*>(&Es[buf][kl]);
+          ee[0] = ev.x;
+          ee[1] = ev.y;
+          ee[2] = ev.z;
+          ee[3] = ev.w;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = rg * 4 + c;
+          float p = fast_exp2(fmaf(sacc[r], sl2, -l2));
+          if (partial) {
+            const int j = j0 + kl + c;
+            const bool live = j <= qi && qi < ee[c] && j < N;
+            p = live ? p : 0.f;
+          }
+          sf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - dii));
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          dqa[db] = mfma32x32x16(tile_frag_t(Ks[buf], kk * 32 + 16 * ks, 32 * db, lane), sf[ks],
+                                 dqa[db]);
+    }
+  };
+
+  LiveTiles it;
+  it.init(emax + static_cast<size_t>(b) * ntiles, (i1 - 1) / KT, i0);
+  int t = it.next();
+  if (t >= 0) {
+    load_tile(t);
+    store_tile(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (t >= 0) {
+    const int tn = it.next();
+    if (tn >= 0) load_tile(tn);
+    const int j0 = t * KT;
+    const bool full = (j0 + KT - 1 <= i0) && (eminb[t] >= i1) && (j0 + KT <= N);
+    compute(buf, j0, !full);
+    if (tn >= 0) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    t = tn;
+  }
+
+  if (qi < N) {
+    bf16_t* op = dq + (static_cast<size_t>(b) * N + qi) * tokq + static_cast<size_t>(hq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = db * 32 + rg * 8 + lh * 4;
+        const f32x16& a = dqa[db];
+        *reinterpret_cast<u32x2*>(op + d) =
+            u32x2{pack_bf16x2(a[rg * 4] * scale, a[rg * 4 + 1] * scale),
+                  pack_bf16x2(a[rg * 4 + 2] * scale, a[rg * 4 + 3] * scale)};
+      }
+  }
+}
+
 size_t di_bytes(int B, int N, int Hq) {
   return (static_cast<size_t>(B) * Hq * N * sizeof(float) + 255) & ~static_cast<size_t>(255);
 }
@@ -512,6 +871,7 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
                                        void* ws, size_t ws_bytes, void* stream) {
   KS_REQUIRE(B >= 0 && N >= 0 && Hq > 0 && Hkv > 0, "ks_evict_attn_bwd: bad sizes");
   KS_REQUIRE(Hq % Hkv == 0, "ks_evict_attn_bwd: Hq %% Hkv != 0");
+  KS_REQUIRE(scale > 0.f, "ks_evict_attn_bwd: scale must be positive");
   if (dtype != KS_BF16 || Dh != D)
     return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_bwd: only bf16 with D=128 (dtype=%d D=%d)",
                    dtype, Dh);
@@ -547,26 +907,24 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   st = ks_check_launch("ks_evict_attn_bwd(pre)");
   if (st != KS_OK) return st;
 
-  const int nkt = (N + KW - 1) / KW;
-  const long long real_kv = static_cast<long long>(B) * Hkv * nkt;
-  const long long total_kv = (real_kv + 7) / 8 * 8;
-  KS_REQUIRE(total_kv < (1LL << 31), "ks_evict_attn_bwd: grid too large");
-  hipLaunchKernelGGL(dkdv_kernel, dim3(static_cast<unsigned>(total_kv)), dim3(256), 0, s, qq, kk,
+  const int nkt = (N + KW8 - 1) / KW8;
+  const long long nkv = static_cast<long long>(B) * Hkv * nkt;
+  KS_REQUIRE(nkv < (1LL << 31), "ks_evict_attn_bwd: grid too large");
+  hipLaunchKernelGGL(dkdv_d128_kernel, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq, kk,
                      vv, e, emin, emax, lse, di, gg, static_cast<bf16_t*>(dk),
-                     static_cast<bf16_t*>(dv), B, N, Hq, Hkv, ntiles, nkt,
-                     static_cast<int>(total_kv), scale);
+                     static_cast<bf16_t*>(dv), B, N, Hq, Hkv, ntiles, scale);
   st = ks_check_launch("ks_evict_attn_bwd(dkdv)");
   if (st != KS_OK) return st;
 
-  const int rs = 4 / hpw;
-  const int nqt = (N + 64 * rs - 1) / (64 * rs);
+  const int rs = 8 / hpw;
+  const int nqt = (N + 32 * rs - 1) / (32 * rs);
   const long long real_q = static_cast<long long>(B) * (Hq / hpw) * nqt;
   const long long total_q = (real_q + 7) / 8 * 8;
   KS_REQUIRE(total_q < (1LL << 31), "ks_evict_attn_bwd: grid too large");
-#define KS_DQ_LAUNCH(HPW_)                                                                     \
-  hipLaunchKernelGGL((dq_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(256), 0, s,  \
-                     qq, kk, vv, e, emin, emax, lse, di, gg, static_cast<bf16_t*>(dq), B, N, Hq, \
-                     Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
+#define KS_DQ_LAUNCH(HPW_)                                                                   \
+  hipLaunchKernelGGL((dq_d128_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(512), \
+                     0, s, qq, kk, vv, e, emin, emax, lse, di, gg, static_cast<bf16_t*>(dq), B, \
+                     N, Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
   if (hpw == 4) KS_DQ_LAUNCH(4);
   else if (hpw == 2) KS_DQ_LAUNCH(2);
   else KS_DQ_LAUNCH(1);

@@ -50,4 +50,63 @@ struct LiveTiles {
   }
 };
 
+// ---------------------------------------------------------------------------
+// LDS tiles of 128-element bf16 rows (D = 128), stored in natural [row][d]
+// order with the 16-byte chunks of row r permuted by chunk ^ swz(r).  The
+// permutation makes both access patterns of the MFMA loops conflict-free:
+//   * 16-byte reads of one chunk from 16 consecutive rows (swz is a bijection
+//     on r mod 16), and
+//   * ds_read_b64_tr_b16 transpose reads, where a 16-lane group reads 4
+//     consecutive rows x 16 consecutive columns (swz moves the 4 rows to
+//     distinct 64-byte groups).
+// ---------------------------------------------------------------------------
+constexpr int kRowElems = 128;
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// element offset of (row, col) in a swizzled tile
+__device__ __forceinline__ int tile_idx(int row, int col) {
+  return row * kRowElems + (((col >> 3) ^ swz(row)) << 3) + (col & 7);
+}
+
+// 16-byte chunk `chunk` of row `row`
+__device__ __forceinline__ bf16x8 tile_chunk(const bf16_t* t, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(t + row * kRowElems + ((chunk ^ swz(row)) << 3));
+}
+
+__device__ __forceinline__ void tile_store_chunk(bf16_t* t, int row, int chunk, u32x4 v) {
+  *reinterpret_cast<u32x4*>(t + row * kRowElems + ((chunk ^ swz(row)) << 3)) = v;
+}
+
+__device__ __forceinline__ bf16x4 lds_tr16(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(p));
+}
+
+// A operand of a 32x32x16 MFMA that contracts over tile ROWS: lane l gets
+// X[k(v)][dbase + l % 32] for v = 0..7 with
+//   k(v) = r0 + 8 * (v / 4) + 4 * (l / 32) + v % 4,
+// the k order in which a 32x32 accumulator holds its rows (so P^T / dS^T
+// taken straight from an S accumulator is the matching B operand).
+// ds_read_b64_tr_b16 semantics: within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte reads of lanes 4r + i / 4, r = 0..3.
+__device__ __forceinline__ bf16x8 tile_frag_t(const bf16_t* t, int r0, int dbase, int lane) {
+  const int j = lane & 15, g = lane >> 4, h = lane >> 5;
+  const int row = r0 + 4 * h + (j >> 2);
+  const int col = dbase + 16 * (g & 1) + 4 * (j & 3);
+  const bf16x4 lo = lds_tr16(t + tile_idx(row, col));
+  const bf16x4 hi = lds_tr16(t + tile_idx(row + 8, col));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// acc + sum of the 8 bf16 values (packed dot products with (1, 1))
+__device__ __forceinline__ float sum_bf16x8(bf16x8 x, float acc) {
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
+  return acc;
+}
+
 }  // namespace ksattn

@@ -413,6 +413,200 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 forward, D = 128 (MFMA, 8 waves)
+//
+// A workgroup = 8 waves = HPW query heads x 8/HPW subtiles of 32 query rows,
+// so every staged 64-key tile is shared by 8 waves and each SIMD runs 2 waves
+// (register budget <= 256), letting one wave's MFMAs overlap the other's
+// softmax.  K and V stay in natural [key][d] layout in LDS; V^T operands are
+// read with the LDS transpose instruction, so staging is a plain 16-byte copy.
+// Per key tile and wave: S^T = K Q^T (16 MFMAs), masked lazily-rescaled
+// softmax on 32 scores per lane, O^T += V^T P^T (16 MFMAs).
+// ---------------------------------------------------------------------------
+template <int HPW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_d128_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
+    const int32_t* __restrict__ emax, bf16_t* __restrict__ o, float* __restrict__ lse, int B,
+    int N, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float sl2) {
+  constexpr int D = 128;
+  constexpr int RS = 8 / HPW;   // 32-row subtiles per workgroup
+  constexpr int BM = 32 * RS;   // query rows per workgroup
+  constexpr int KT = kKeyTile;  // 64 keys per tile
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * D];
+  __shared__ __attribute__((aligned(16))) int Es[2][KT];
+
+  int lin = blockIdx.x;
+  lin = (lin & 7) * (total_wg >> 3) + (lin >> 3);
+  const int ngrp = Hq / HPW;
+  if (lin >= B * ngrp * nqt) return;
+  const int qt = lin % nqt;
+  const int grp = (lin / nqt) % ngrp;
+  const int b = lin / (nqt * ngrp);
+  const int G = Hq / Hkv;
+  const int hq0 = grp * HPW;
+  const int hkv = hq0 / G;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int hq = hq0 + (w % HPW);
+  const int i0 = qt * BM;
+  const int wi0 = i0 + (w / HPW) * 32;
+  const int i1 = min(N, i0 + BM);
+  const int lq = lane & 31, lh = lane >> 5;
+  const int qi = wi0 + lq;  // this lane's query row
+
+  const size_t tok = static_cast<size_t>(Hkv) * D;
+  const bf16_t* kb = k + static_cast<size_t>(b) * N * tok + static_cast<size_t>(hkv) * D;
+  const bf16_t* vb = v + static_cast<size_t>(b) * N * tok + static_cast<size_t>(hkv) * D;
+  const int32_t* eb = e + static_cast<size_t>(b) * N;
+  const int32_t* eminb = emin + static_cast<size_t>(b) * ntiles;
+
+  // Q as the B operand of S^T = K Q^T: row qi, d = 16 s + 8 lh .. +8
+  bf16x8 qf[8];
+  {
+    const bf16_t* qp = q + (static_cast<size_t>(b) * N + (qi < N ? qi : 0)) * Hq * D +
+                       static_cast<size_t>(hq) * D + lh * 8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(qp + s * 16);
+      if (qi >= N) x = u32x4{0u, 0u, 0u, 0u};
+      qf[s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float mrow = -1e30f, lrow = 0.f;
+
+  // staging: 2 K chunks + 2 V chunks of 16 bytes per thread per tile
+  u32x4 kr[2], vr[2];
+  int er = 0;
+  auto load_tile = [&](int t) {
+    const int j0 = t * KT;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 512 * u;
+      const int row = idx >> 4, c = idx & 15;
+      const int j = j0 + row;
+      const bool ok = j < N;
+      kr[u] = ok ? *reinterpret_cast<const u32x4*>(kb + j * tok + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      vr[u] = ok ? *reinterpret_cast<const u32x4*>(vb + j * tok + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < KT) er = (j0 + tid < N) ? eb[j0 + tid] : 0;
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 512 * u;
+      tile_store_chunk(Ks[buf], idx >> 4, idx & 15, kr[u]);
+      tile_store_chunk(Vs[buf], idx >> 4, idx & 15, vr[u]);
+    }
+    if (tid < KT) Es[buf][tid] = er;
+  };
+
+  auto compute = [&](int buf, int j0, bool partial) {
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kk][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        sacc[kk] = mfma32x32x16(tile_chunk(Ks[buf], kk * 32 + lq, 2 * s + lh), qf[s], sacc[kk]);
+    }
+    if (partial) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int kl = kk * 32 + rg * 8 + lh * 4;
+          const int4 ev = *reinterpret_cast<const int4*>(&Es[buf][kl]);
+          const int ee[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int j = j0 + kl + c;
+            const bool live = j <= qi && qi < ee[c] && j < N;
+            sacc[kk][rg * 4 + c] = live ? sacc[kk][rg * 4 + c] : -INFINITY;
+          }
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kk][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    const bool need = mx > mrow + kTau;
+    if (__ballot(need)) {
+      const float f = need ? fast_exp2(mrow - mx) : 1.f;
+      mrow = need ? mx : mrow;
+      lrow *= f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= f;
+    }
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 pk;
+#pragma unroll
+        for (int vv = 0; vv < 8; ++vv)
+          pk[vv] = (__bf16)fast_exp2(fmaf(sacc[kk][ks * 8 + vv], sl2, -mrow));
+        pf[kk * 2 + ks] = pk;
+        lrow = sum_bf16x8(pk, lrow);
+      }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        oacc[db] = mfma32x32x16(tile_frag_t(Vs[buf], kk * 16, db * 32, lane), pf[kk], oacc[db]);
+  };
+
+  LiveTiles it;
+  it.init(emax + static_cast<size_t>(b) * ntiles, (i1 - 1) / KT, i0);
+  int t = it.next();
+  if (t >= 0) {
+    load_tile(t);
+    store_tile(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (t >= 0) {
+    const int tn = it.next();
+    if (tn >= 0) load_tile(tn);
+    const int j0 = t * KT;
+    const bool full = (j0 + KT - 1 <= i0) && (eminb[t] >= i1) && (j0 + KT <= N);
+    compute(buf, j0, !full);
+    if (tn >= 0) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    t = tn;
+  }
+
+  const float lt = lrow + __shfl_xor(lrow, 32);
+  if (qi < N) {
+    const float inv = 1.f / lt;
+    bf16_t* op = o + (static_cast<size_t>(b) * N + qi) * Hq * D + static_cast<size_t>(hq) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = db * 32 + rg * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(op + d) =
+            u32x2{pack_bf16x2(oacc[db][rg * 4 + 0] * inv, oacc[db][rg * 4 + 1] * inv),
+                  pack_bf16x2(oacc[db][rg * 4 + 2] * inv, oacc[db][rg * 4 + 3] * inv)};
+      }
+    if (lse && lh == 0)
+      lse[(static_cast<size_t>(b) * Hq + hq) * N + qi] = (mrow + __log2f(lt)) * KS_LN2;
+  }
+}
+
 }  // namespace
 }  // namespace ksattn
 
@@ -434,6 +628,7 @@ extern "C" ks_status ks_evict_attn_fwd(const void* q, const void* k, const void*
   KS_REQUIRE(B >= 0 && N >= 0 && Hq > 0 && Hkv > 0, "ks_evict_attn_fwd: bad sizes");
   KS_REQUIRE(Hq % Hkv == 0, "ks_evict_attn_fwd: Hq %% Hkv != 0");
   KS_REQUIRE(dtype == KS_F32 || dtype == KS_BF16, "ks_evict_attn_fwd: dtype %d", dtype);
+  KS_REQUIRE(scale > 0.f, "ks_evict_attn_fwd: scale must be positive");
   const int G = Hq / Hkv;
   if (dtype == KS_BF16 && !(D == 128 || D == 64))
     return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_fwd: bf16 needs D=64 or 128 (D=%d)", D);
@@ -484,9 +679,19 @@ extern "C" ks_status ks_evict_attn_fwd(const void* q, const void* k, const void*
                      dim3(256), 0, s, qq, kk, vv, e, emin, emax, oo, lse, B, N, Hq, Hkv,      \
                      ntiles, nqt, static_cast<int>(total), sl2)
   if (D == 128) {
-    if (hpw == 4) KS_FWD_LAUNCH(128, 4);
-    else if (hpw == 2) KS_FWD_LAUNCH(128, 2);
-    else KS_FWD_LAUNCH(128, 1);
+    const int rs8 = 8 / hpw;
+    const int nqt8 = (N + 32 * rs8 - 1) / (32 * rs8);
+    const long long real8 = static_cast<long long>(B) * (Hq / hpw) * nqt8;
+    const long long total8 = (real8 + 7) / 8 * 8;
+    KS_REQUIRE(total8 < (1LL << 31), "ks_evict_attn_fwd: grid too large");
+#define KS_FWD128_LAUNCH(HPW_)                                                                 \
+  hipLaunchKernelGGL((fwd_d128_kernel<HPW_>), dim3(static_cast<unsigned>(total8)), dim3(512), 0, \
+                     s, qq, kk, vv, e, emin, emax, oo, lse, B, N, Hq, Hkv, ntiles, nqt8,          \
+                     static_cast<int>(total8), sl2)
+    if (hpw == 4) KS_FWD128_LAUNCH(4);
+    else if (hpw == 2) KS_FWD128_LAUNCH(2);
+    else KS_FWD128_LAUNCH(1);
+#undef KS_FWD128_LAUNCH
   } else {
     if (hpw == 4) KS_FWD_LAUNCH(64, 4);
     else if (hpw == 2) KS_FWD_LAUNCH(64, 2);
