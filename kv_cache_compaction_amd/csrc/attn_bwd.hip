@@ -6,17 +6,17 @@
 //   dS = P o (dP - D_i), dQ = scale dS K, dK = scale dS^T Q.
 //
 // Deterministic two-kernel split (no atomics, no fp32 dQ workspace):
-//   dkdv_kernel  key-tile outer.  A workgroup owns 128 keys of one kv head
-//                (32 per wave, K and V held in registers as MFMA operands)
-//                and walks every query head of the group over the query
-//                rows that can see those keys, [j0, max e_j).  Per 32-query
-//                chunk staged in LDS (natural and transposed): S = Q K^T,
-//                dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS  (4 MFMA GEMMs).
-//   dq_kernel    query-tile outer, laid out like the forward (64 rows per
-//                wave, key tiles staged in LDS, live tiles found by ballot):
-//                S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (3 GEMMs).
+//   dkdv_kernel  key-tile outer: a workgroup owns 256 keys of one kv head and
+//                walks every query head of the group over the query rows
+//                that can see them, [j0, max e_j), in 32-row chunks:
+//                S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
+//   dq_kernel    query-tile outer, laid out like the forward:
+//                S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
 // The pair executes 14*D flops per live (query, key, head) triple against
 // the 10*D of a fused kernel, in exchange for no atomic traffic at all.
+// Both run 8 waves per workgroup (2 per SIMD) on tiles staged in natural
+// layout (see attn_common.h); transposed operands come from LDS transpose
+// reads, and the element mask runs only on partial tiles (uniform branch).
 #include "attn_common.h"
 
 namespace ksattn {
@@ -26,6 +26,9 @@ constexpr int D = 128;
 constexpr int NSTEP = D / 16;  // k-steps over the head dimension
 constexpr int NDB = D / 32;    // 32-wide d blocks
 constexpr int CH = D / 8;      // 16-byte chunks per row
+constexpr int BQ = 32;         // query rows per dK/dV chunk
+constexpr int KW = 256;        // keys per dK/dV workgroup (8 waves x 32)
+constexpr int KT = kKeyTile;   // keys per dQ tile
 
 // ---------------------------------------------------------------------------
 // D_i = sum_d dO_id O_id  (fp32), and LSE in log2 units
@@ -56,458 +59,22 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__
   }
 }
 
-// slot of the first of 4 consecutive rows (4*g) in the MFMA k order: bits 2
-// and 3 of the row index swapped within each 16-row group
-__device__ __forceinline__ int quad_slot(int g) {
-  return 16 * (g >> 2) + 8 * (g & 1) + 4 * ((g >> 1) & 1);
-}
-
-// 4 rows x 8 bf16 (u32x4 each) -> for column dd, the 4 values as 2 packed words
-__device__ __forceinline__ u32x2 column4(const u32x4 (&x)[4], int dd) {
-  const int ws = dd >> 1;
-  if (dd & 1)
-    return u32x2{(x[0][ws] >> 16) | (x[1][ws] & 0xffff0000u),
-                 (x[2][ws] >> 16) | (x[3][ws] & 0xffff0000u)};
-  return u32x2{(x[0][ws] & 0xffffu) | (x[1][ws] << 16), (x[2][ws] & 0xffffu) | (x[3][ws] << 16)};
-}
-
 // ---------------------------------------------------------------------------
-// dK, dV: key-tile outer
+// dK, dV.  K stays in registers as the B operand of S = Q K^T; V of the 256
+// keys stays in LDS for the whole walk (B operand of dP = dO V^T).  Query
+// chunks are staged once per workgroup; dO^T and Q^T come from transpose
+// reads.  Workgroups are ordered key-tile major so the heavy prompt tiles
+// (whose queries run to the end of the trace) start first.
 // ---------------------------------------------------------------------------
-constexpr int KW = 128;  // keys per workgroup (4 waves x 32)
-constexpr int BQ = 32;   // query rows per chunk
-
-__global__ __launch_bounds__(256) void dkdv_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
-    const int32_t* __restrict__ emax, const float* __restrict__ lse,
-    const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk,
-    bf16_t* __restrict__ dv, int B, int N, int Hq, int Hkv, int ntiles, int nkt, int total_wg,
-    float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Os[2][BQ * D];   // dO natural
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[2][D * BQ];
-  __shared__ __attribute__((aligned(16))) bf16_t Ot[2][D * BQ];   // dO transposed
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
-
-  int lin = blockIdx.x;
-  lin = (lin & 7) * (total_wg >> 3) + (lin >> 3);
-  if (lin >= B * Hkv * nkt) return;
-  const int kt = lin % nkt;
-  const int hkv = (lin / nkt) % Hkv;
-  const int b = lin / (nkt * Hkv);
-  const int G = Hq / Hkv;
-
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int lq = lane & 31, lh = lane >> 5;
-  const int j0 = kt * KW;
-  const int kw0 = j0 + 32 * w;
-  const int jl = kw0 + lq;  // this lane's key
-  const size_t tokkv = static_cast<size_t>(Hkv) * D;
-  const size_t tokq = static_cast<size_t>(Hq) * D;
-
-  // K^T / V^T as B operands: lane holds row jl, d = 16*step + 8*lh .. +8
-  bf16x8 kf[NSTEP], vf[NSTEP];
-  {
-    const size_t off = (static_cast<size_t>(b) * N + (jl < N ? jl : 0)) * tokkv +
-                       static_cast<size_t>(hkv) * D + lh * 8;
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      u32x4 a = *reinterpret_cast<const u32x4*>(k + off + s * 16);
-      u32x4 c = *reinterpret_cast<const u32x4*>(v + off + s * 16);
-      if (jl >= N) a = c = u32x4{0u, 0u, 0u, 0u};
-      kf[s] = __builtin_bit_cast(bf16x8, a);
-      vf[s] = __builtin_bit_cast(bf16x8, c);
-    }
-  }
-  const int ej = jl < N ? e[static_cast<size_t>(b) * N + jl] : 0;
-
-  // query range of the workgroup and of this wave
-  const int t0 = j0 / kKeyTile;
-  const int t1 = min(ntiles - 1, t0 + KW / kKeyTile - 1);
-  int emx = 0x80000000, emn = 0x7fffffff;
-  for (int t = t0; t <= t1; ++t) {
-    emx = max(emx, emax[static_cast<size_t>(b) * ntiles + t]);
-    emn = min(emn, emin[static_cast<size_t>(b) * ntiles + t]);
-  }
-  const int qend = min(N, emx);  // exclusive
-  // wave-level range (uniform): keys [kw0, kw0 + 32), max e over them
-  int wemx = jl < N ? ej : static_cast<int>(0x80000000);
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) wemx = max(wemx, __shfl_xor(wemx, off));
-  const int wq1 = min(N, wemx);
-  const int kmax = min(N, j0 + KW) - 1;  // last existing key of the workgroup
-
-  f32x16 dka[NDB], dva[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dka[db][r] = dva[db][r] = 0.f;
-
-  const float sl2 = scale * KS_LOG2E;
-  // staging registers: threads 0..127 handle Q, 128..255 handle dO; each a
-  // (4-row group, 16-byte d chunk) pair
-  const int half = tid >> 7;
-  const int pr = tid & 127;
-  const int qg = pr & 7, dc = pr >> 3;
-  u32x4 xr[4];
-  float lr = 0.f;
-
-  const int c_begin = j0 / BQ;
-  const int c_end = (qend + BQ - 1) / BQ;  // exclusive
-  const int nchunks = c_end > c_begin ? (c_end - c_begin) * G : 0;
-
-  auto load_chunk = [&](int idx) {
-    const int h = hkv * G + idx / (c_end - c_begin);
-    const int c0 = (c_begin + idx % (c_end - c_begin)) * BQ;
-    const bf16_t* src = half ? dout : q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = c0 + 4 * qg + i;
-      xr[i] = row < N ? *reinterpret_cast<const u32x4*>(
-                            src + (static_cast<size_t>(b) * N + row) * tokq +
-                            static_cast<size_t>(h) * D + dc * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < 2 * BQ) {
-      const int row = c0 + (tid & (BQ - 1));
-      const size_t li = (static_cast<size_t>(b) * Hq + h) * N + row;
-      if (tid < BQ)
-        lr = row < N ? lse[li] * KS_LOG2E : INFINITY;
-      else
-        lr = row < N ? di[li] : 0.f;
-    }
-  };
-  auto store_chunk = [&](int buf) {
-    bf16_t* nat = half ? Os[buf] : Qs[buf];
-    bf16_t* tr = half ? Ot[buf] : Qt[buf];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * qg + i;
-      *reinterpret_cast<u32x4*>(&nat[row * D + ((dc ^ (row & (CH - 1))) * 8)]) = xr[i];
-    }
-    const int slot = quad_slot(qg);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int d = dc * 8 + dd;
-      const int chunk = (slot >> 3) ^ ((d >> 2) & 3);
-      *reinterpret_cast<u32x2*>(&tr[d * BQ + chunk * 8 + (slot & 7)]) = column4(xr, dd);
-    }
-    if (tid < BQ)
-      Ls[buf][tid] = lr;
-    else if (tid < 2 * BQ)
-      Ds[buf][tid - BQ] = lr;
-  };
-
-  auto compute = [&](int buf, int c0) {
-    // skip chunks none of this wave's keys can see (uniform per wave)
-    if (c0 >= wq1 || c0 + BQ <= kw0) return;
-    const bool full = (c0 >= kmax) && (c0 + BQ <= emn) && (c0 + BQ <= N);
-    f32x16 sacc, pacc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      const int c = 2 * s + lh;
-      const int off = lq * D + ((c ^ (lq & (CH - 1))) * 8);
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&Qs[buf][off]);
-      const bf16x8 gf = *reinterpret_cast<const bf16x8*>(&Os[buf][off]);
-      sacc = mfma32x32x16(af, kf[s], sacc);  // S[q][key]:  lane col = key
-      pacc = mfma32x32x16(gf, vf[s], pacc);  // dP[q][key]
-    }
-    bf16x8 pf[2], sf[2];
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int ql = rg * 8 + lh * 4;
-      const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][ql]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&Ds[buf][ql]);
-      const float la[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float da[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int r = rg * 4 + c;
-        float p = fast_exp2(sacc[r] * sl2 - la[c]);
-        if (!full) {
-          const int i = c0 + ql + c;
-          const bool live = jl <= i && i < ej && i < N && jl < N;
-          p = live ? p : 0.f;
-        }
-        const float ds = p * (pacc[r] - da[c]);
-        pf[r >> 3][r & 7] = (__bf16)p;
-        sf[r >> 3][r & 7] = (__bf16)ds;
-      }
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 32 + lq;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int chunk = (2 * ks + lh) ^ ((d >> 2) & 3);
-        const bf16x8 of = *reinterpret_cast<const bf16x8*>(&Ot[buf][d * BQ + chunk * 8]);
-        const bf16x8 qtf = *reinterpret_cast<const bf16x8*>(&Qt[buf][d * BQ + chunk * 8]);
-        dva[db] = mfma32x32x16(of, pf[ks], dva[db]);   // dV^T[d][key]
-        dka[db] = mfma32x32x16(qtf, sf[ks], dka[db]);  // dK^T[d][key]
-      }
-    }
-  };
-
-  if (nchunks > 0) {
-    load_chunk(0);
-    store_chunk(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int idx = 0; idx < nchunks; ++idx) {
-    const bool more = idx + 1 < nchunks;
-    if (more) load_chunk(idx + 1);
-    compute(buf, (c_begin + idx % (c_end - c_begin)) * BQ);
-    if (more) store_chunk(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-  }
-
-  // epilogue: lane holds key jl; rows of dK^T/dV^T are d = 32db + 8rg + 4lh + c
-  if (jl < N) {
-    const size_t off = (static_cast<size_t>(b) * N + jl) * tokkv + static_cast<size_t>(hkv) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d = db * 32 + rg * 8 + lh * 4;
-        const u32x2 kw = {pack_bf16x2(dka[db][rg * 4] * scale, dka[db][rg * 4 + 1] * scale),
-                          pack_bf16x2(dka[db][rg * 4 + 2] * scale, dka[db][rg * 4 + 3] * scale)};
-        const u32x2 vw = {pack_bf16x2(dva[db][rg * 4], dva[db][rg * 4 + 1]),
-                          pack_bf16x2(dva[db][rg * 4 + 2], dva[db][rg * 4 + 3])};
-        *reinterpret_cast<u32x2*>(dk + off + d) = kw;
-        *reinterpret_cast<u32x2*>(dv + off + d) = vw;
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dQ: query-tile outer
-// ---------------------------------------------------------------------------
-constexpr int KT = kKeyTile;
-
-template <int HPW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dq_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
-    const int32_t* __restrict__ emax, const float* __restrict__ lse,
-    const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
-    int B, int N, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale) {
-  constexpr int RS = 4 / HPW;
-  constexpr int BM = 64 * RS;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[2][D * KT];
-  __shared__ __attribute__((aligned(16))) int Es[2][KT];
-
-  int lin = blockIdx.x;
-  lin = (lin & 7) * (total_wg >> 3) + (lin >> 3);
-  const int ngrp = Hq / HPW;
-  if (lin >= B * ngrp * nqt) return;
-  const int qt = lin % nqt;
-  const int grp = (lin / nqt) % ngrp;
-  const int b = lin / (nqt * ngrp);
-  const int G = Hq / Hkv;
-  const int hq0 = grp * HPW;
-  const int hkv = hq0 / G;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int hq = hq0 + (w % HPW);
-  const int i0 = qt * BM;
-  const int wi0 = i0 + (w / HPW) * 64;
-  const int i1 = min(N, i0 + BM);
-  const int lq = lane & 31, lh = lane >> 5;
-  const size_t tokkv = static_cast<size_t>(Hkv) * D;
-  const size_t tokq = static_cast<size_t>(Hq) * D;
-  const bf16_t* kb = k + static_cast<size_t>(b) * N * tokkv + static_cast<size_t>(hkv) * D;
-  const bf16_t* vb = v + static_cast<size_t>(b) * N * tokkv + static_cast<size_t>(hkv) * D;
-  const int32_t* eb = e + static_cast<size_t>(b) * N;
-  const int32_t* eminb = emin + static_cast<size_t>(b) * ntiles;
-  const float sl2 = scale * KS_LOG2E;
-
-  bf16x8 qf[2][NSTEP], gf[2][NSTEP];
-  float l2[2], dii[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = wi0 + qb * 32 + lq;
-    const size_t off = (static_cast<size_t>(b) * N + (row < N ? row : 0)) * tokq +
-                       static_cast<size_t>(hq) * D + lh * 8;
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      u32x4 a = *reinterpret_cast<const u32x4*>(q + off + s * 16);
-      u32x4 c = *reinterpret_cast<const u32x4*>(dout + off + s * 16);
-      if (row >= N) a = c = u32x4{0u, 0u, 0u, 0u};
-      qf[qb][s] = __builtin_bit_cast(bf16x8, a);
-      gf[qb][s] = __builtin_bit_cast(bf16x8, c);
-    }
-    const size_t li = (static_cast<size_t>(b) * Hq + hq) * N + (row < N ? row : 0);
-    l2[qb] = row < N ? lse[li] * KS_LOG2E : INFINITY;
-    dii[qb] = row < N ? di[li] : 0.f;
-  }
-  f32x16 dqa[2][NDB];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dqa[qb][db][r] = 0.f;
-
-  // staging: thread = (4-key group kg, d chunk dc) pair; 16 x 16 = 256 pairs
-  const int kg = tid & 15, dc = tid >> 4;
-  u32x4 kr[4], vr[4];
-  int er = 0;
-  auto load_tile = [&](int t) {
-    const int j0 = t * KT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = j0 + 4 * kg + i;
-      const bool ok = j < N;
-      kr[i] = ok ? *reinterpret_cast<const u32x4*>(kb + j * tokkv + dc * 8) : u32x4{0u, 0u, 0u, 0u};
-      vr[i] = ok ? *reinterpret_cast<const u32x4*>(vb + j * tokkv + dc * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < KT) er = (j0 + tid < N) ? eb[j0 + tid] : 0;
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * kg + i;
-      const int o = row * D + ((dc ^ (row & (CH - 1))) * 8);
-      *reinterpret_cast<u32x4*>(&Ks[buf][o]) = kr[i];
-      *reinterpret_cast<u32x4*>(&Vs[buf][o]) = vr[i];
-    }
-    const int slot = quad_slot(kg);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int d = dc * 8 + dd;
-      const int chunk = (slot >> 3) ^ ((d >> 1) & 7);
-      *reinterpret_cast<u32x2*>(&Kt[buf][d * KT + chunk * 8 + (slot & 7)]) = column4(kr, dd);
-    }
-    if (tid < KT) Es[buf][tid] = er;
-  };
-
-  auto compute = [&](int buf, int j0, bool partial) {
-#pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk) {
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[0][r] = sacc[1][r] = pacc[0][r] = pacc[1][r] = 0.f;
-      const int krow = kbk * 32 + lq;
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        const int c = 2 * s + lh;
-        const int off = krow * D + ((c ^ (krow & (CH - 1))) * 8);
-        const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&Ks[buf][off]);
-        const bf16x8 vfr = *reinterpret_cast<const bf16x8*>(&Vs[buf][off]);
-        sacc[0] = mfma32x32x16(kfr, qf[0][s], sacc[0]);  // S^T[key][q]
-        sacc[1] = mfma32x32x16(kfr, qf[1][s], sacc[1]);
-        pacc[0] = mfma32x32x16(vfr, gf[0][s], pacc[0]);  // dP^T[key][q]
-        pacc[1] = mfma32x32x16(vfr, gf[1][s], pacc[1]);
-      }
-      bf16x8 sf[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int i = wi0 + qb * 32 + lq;
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int kl = kbk * 32 + rg * 8 + lh * 4;
-          int ee[4] = {0, 0, 0, 0};
-          if (partial) {
-            const int4 ev = *reinterpret_cast<const int4*>(&Es[buf][kl]);
-            ee[0] = ev.x;
-            ee[1] = ev.y;
-            ee[2] = ev.z;
-            ee[3] = ev.w;
-          }
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = rg * 4 + c;
-            float p = fast_exp2(sacc[qb][r] * sl2 - l2[qb]);
-            if (partial) {
-              const int j = j0 + kl + c;
-              const bool live = j <= i && i < ee[c] && j < N;
-              p = live ? p : 0.f;
-            }
-            sf[qb][r >> 3][r & 7] = (__bf16)(p * (pacc[qb][r] - dii[qb]));
-          }
-        }
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = db * 32 + lq;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int chunk = (4 * kbk + 2 * ks + lh) ^ ((d >> 1) & 7);
-          const bf16x8 ktf = *reinterpret_cast<const bf16x8*>(&Kt[buf][d * KT + chunk * 8]);
-          dqa[0][db] = mfma32x32x16(ktf, sf[0][ks], dqa[0][db]);  // dQ^T[d][q]
-          dqa[1][db] = mfma32x32x16(ktf, sf[1][ks], dqa[1][db]);
-        }
-      }
-    }
-  };
-
-  LiveTiles it;
-  it.init(emax + static_cast<size_t>(b) * ntiles, (i1 - 1) / KT, i0);
-  int t = it.next();
-  if (t >= 0) {
-    load_tile(t);
-    store_tile(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (t >= 0) {
-    const int tn = it.next();
-    if (tn >= 0) load_tile(tn);
-    const int j0 = t * KT;
-    const bool full = (j0 + KT - 1 <= i0) && (eminb[t] >= i1) && (j0 + KT <= N);
-    compute(buf, j0, !full);
-    if (tn >= 0) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    t = tn;
-  }
-
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int i = wi0 + qb * 32 + lq;
-    if (i < N) {
-      bf16_t* op = dq + (static_cast<size_t>(b) * N + i) * tokq + static_cast<size_t>(hq) * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int d = db * 32 + rg * 8 + lh * 4;
-          const f32x16& a = dqa[qb][db];
-          *reinterpret_cast<u32x2*>(op + d) =
-              u32x2{pack_bf16x2(a[rg * 4] * scale, a[rg * 4 + 1] * scale),
-                    pack_bf16x2(a[rg * 4 + 2] * scale, a[rg * 4 + 3] * scale)};
-        }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dK, dV (8 waves, natural tiles): a workgroup owns 256 keys of one kv head,
-// 32 per wave.  K stays in registers as the B operand of S = Q K^T; V of the
-// 256 keys stays in LDS for the whole walk (B operand of dP = dO V^T).  Query
-// chunks of 32 rows are staged once, in natural layout; the transposed
-// operands of dV^T += dO^T P and dK^T += Q^T dS come from transpose reads.
-// Workgroups are ordered key-tile major so the heavy prompt tiles (whose
-// queries run to the end of the trace) start first.
-// ---------------------------------------------------------------------------
-constexpr int KW8 = 256;
-
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_d128_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
     const int32_t* __restrict__ emax, const float* __restrict__ lse,
     const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk,
     bf16_t* __restrict__ dv, int B, int N, int Hq, int Hkv, int ntiles, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t Vst[KW8 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Os[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vst[KW * kTileRow];
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * kTileRow];
+  __shared__ __attribute__((aligned(16))) bf16_t Os[2][BQ * kTileRow];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
@@ -518,7 +85,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lh = lane >> 5;
-  const int j0 = kt * KW8;
+  const int la = tile_lane_a(lane), lt = tile_lane_t(lane);
+  const int j0 = kt * KW;
   const int kw0 = j0 + 32 * w;
   const int jl = kw0 + lq;
   const size_t tokkv = static_cast<size_t>(Hkv) * D;
@@ -537,8 +105,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   const int ej = jl < N ? e[static_cast<size_t>(b) * N + jl] : 0;
-  // V of the workgroup's keys, staged once
-  for (int idx = tid; idx < KW8 * CH; idx += 512) {
+  for (int idx = tid; idx < KW * CH; idx += 512) {
     const int row = idx >> 4, c = idx & 15;
     const int j = j0 + row;
     const u32x4 x = j < N ? *reinterpret_cast<const u32x4*>(
@@ -549,18 +116,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   const int t0 = j0 / kKeyTile;
-  const int t1 = min(ntiles - 1, t0 + KW8 / kKeyTile - 1);
+  const int t1 = min(ntiles - 1, t0 + KW / kKeyTile - 1);
   int emx = static_cast<int>(0x80000000), emn = 0x7fffffff;
   for (int t = t0; t <= t1; ++t) {
     emx = max(emx, emax[static_cast<size_t>(b) * ntiles + t]);
     emn = min(emn, emin[static_cast<size_t>(b) * ntiles + t]);
   }
+  // workgroup / wave bounds, made provably uniform for the compiler
+  emx = __builtin_amdgcn_readfirstlane(emx);
+  emn = __builtin_amdgcn_readfirstlane(emn);
   const int qend = min(N, emx);
   int wemx = jl < N ? ej : static_cast<int>(0x80000000);
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) wemx = max(wemx, __shfl_xor(wemx, off));
-  const int wq1 = min(N, wemx);
-  const int kmax = min(N, j0 + KW8) - 1;
+  const int wq1 = __builtin_amdgcn_readfirstlane(min(N, wemx));
+  const int kmax = min(N, j0 + KW) - 1;
 
   f32x16 dka[NDB], dva[NDB];
 #pragma unroll
@@ -606,43 +176,59 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   auto compute = [&](int buf, int c0) {
     if (c0 >= wq1 || c0 + BQ <= kw0) return;  // none of this wave's keys is seen
-    const bool full = (c0 >= kmax) && (c0 + BQ <= emn) && (c0 + BQ <= N);
+    const bool partial = !((c0 >= kmax) && (c0 + BQ <= emn) && (c0 + BQ <= N));
     f32x16 sacc, pacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      sacc = mfma32x32x16(tile_chunk(Qs[buf], lq, 2 * s + lh), kf[s], sacc);
-      pacc = mfma32x32x16(tile_chunk(Os[buf], lq, 2 * s + lh),
-                          tile_chunk(Vst, 32 * w + lq, 2 * s + lh), pacc);
+      sacc = mfma32x32x16(tile_chunk(Qs[buf], la, 0, 2 * s + lh), kf[s], sacc);
+      pacc = mfma32x32x16(tile_chunk(Os[buf], la, 0, 2 * s + lh),
+                          tile_chunk(Vst, la, 32 * w, 2 * s + lh), pacc);
+    }
+    // lane = key jl; accumulator row r = query c0 + 8 (r / 4) + 4 lh + r % 4
+    float pv[16];
+    if (partial) {  // uniform branch: element mask only on partial chunks
+      const int lo = jl - c0, hi = min(ej, N) - c0;  // live iff lo <= row < hi
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][rg * 8 + lh * 4]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int row = rg * 8 + lh * 4 + c;
+          const float p = fast_exp2(fmaf(sacc[rg * 4 + c], sl2, -lv[c]));
+          pv[rg * 4 + c] = (row >= lo && row < hi) ? p : 0.f;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][rg * 8 + lh * 4]);
+        pv[rg * 4 + 0] = fast_exp2(fmaf(sacc[rg * 4 + 0], sl2, -l4.x));
+        pv[rg * 4 + 1] = fast_exp2(fmaf(sacc[rg * 4 + 1], sl2, -l4.y));
+        pv[rg * 4 + 2] = fast_exp2(fmaf(sacc[rg * 4 + 2], sl2, -l4.z));
+        pv[rg * 4 + 3] = fast_exp2(fmaf(sacc[rg * 4 + 3], sl2, -l4.w));
+      }
     }
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      const int ql = rg * 8 + lh * 4;
-      const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][ql]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&Ds[buf][ql]);
-      const float la[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+      const float4 d4 = *reinterpret_cast<const float4*>(&Ds[buf][rg * 8 + lh * 4]);
+      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int r = rg * 4 + c;
-        float p = fast_exp2(fmaf(sacc[r], sl2, -la[c]));
-        if (!full) {
-          const int i = c0 + ql + c;
-          const bool live = jl <= i && i < ej && i < N && jl < N;
-          p = live ? p : 0.f;
-        }
-        pf[r >> 3][r & 7] = (__bf16)p;
-        sf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - da[c]));
+        pf[r >> 3][r & 7] = (__bf16)pv[r];
+        sf[r >> 3][r & 7] = (__bf16)(pv[r] * (pacc[r] - dd[c]));
       }
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        dva[db] = mfma32x32x16(tile_frag_t(Os[buf], 16 * ks, 32 * db, lane), pf[ks], dva[db]);
-        dka[db] = mfma32x32x16(tile_frag_t(Qs[buf], 16 * ks, 32 * db, lane), sf[ks], dka[db]);
+        dva[db] = mfma32x32x16(tile_frag_t(Os[buf], lt, 16 * ks, 32 * db), pf[ks], dva[db]);
+        dka[db] = mfma32x32x16(tile_frag_t(Qs[buf], lt, 16 * ks, 32 * db), sf[ks], dka[db]);
       }
   };
 
@@ -661,6 +247,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     buf ^= 1;
   }
 
+  // lane holds key jl; rows of dK^T / dV^T are d = 32 db + 8 rg + 4 lh + c
   if (jl < N) {
     const size_t off = (static_cast<size_t>(b) * N + jl) * tokkv + static_cast<size_t>(hkv) * D;
 #pragma unroll
@@ -679,11 +266,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// dQ (8 waves, natural tiles): laid out like the forward, 32 query rows per
-// wave; K and V key tiles staged natural, K^T operands by transpose reads.
+// dQ: laid out like the forward, 32 query rows per wave; key tiles of K and
+// V staged natural, K^T operands by transpose reads.
 // ---------------------------------------------------------------------------
 template <int HPW>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_d128_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
     const int32_t* __restrict__ emax, const float* __restrict__ lse,
@@ -691,8 +278,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int B, int N, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale) {
   constexpr int RS = 8 / HPW;
   constexpr int BM = 32 * RS;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * kTileRow];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * kTileRow];
   __shared__ __attribute__((aligned(16))) int Es[2][KT];
 
   int lin = blockIdx.x;
@@ -711,6 +298,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wi0 = i0 + (w / HPW) * 32;
   const int i1 = min(N, i0 + BM);
   const int lq = lane & 31, lh = lane >> 5;
+  const int la = tile_lane_a(lane), lt = tile_lane_t(lane);
   const int qi = wi0 + lq;
   const size_t tokkv = static_cast<size_t>(Hkv) * D;
   const size_t tokq = static_cast<size_t>(Hq) * D;
@@ -767,7 +355,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (tid < KT) Es[buf][tid] = er;
   };
 
-  auto compute = [&](int buf, int j0, bool partial) {
+  auto body = [&](int buf, int j0, bool partial) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       f32x16 sacc, pacc;
@@ -775,38 +363,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
-        sacc = mfma32x32x16(tile_chunk(Ks[buf], kk * 32 + lq, 2 * s + lh), qf[s], sacc);
-        pacc = mfma32x32x16(tile_chunk(Vs[buf], kk * 32 + lq, 2 * s + lh), gf[s], pacc);
+        sacc = mfma32x32x16(tile_chunk(Ks[buf], la, kk * 32, 2 * s + lh), qf[s], sacc);
+        pacc = mfma32x32x16(tile_chunk(Vs[buf], la, kk * 32, 2 * s + lh), gf[s], pacc);
+      }
+      // lane = query qi; accumulator row r = key j0 + 32 kk + 8 (r / 4) + 4 lh + r % 4
+      float pv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(fmaf(sacc[r], sl2, -l2));
+      if (partial) {  // uniform branch: element mask only on partial tiles
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int kl = kk * 32 + rg * 8 + lh * 4;
+          const int4 ev = *reinterpret_cast<const int4*>(&Es[buf][kl]);
+          const int ee[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int j = j0 + kl + c;
+            pv[rg * 4 + c] = (j <= qi && qi < ee[c] && j < N) ? pv[rg * 4 + c] : 0.f;
+          }
+        }
       }
       bf16x8 sf[2];
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int kl = kk * 32 + rg * 8 + lh * 4;
-        int ee[4] = {0, 0, 0, 0};
-        if (partial) {
-          const int4 ev = *reinterpret_cast<const int4*>(&Es[buf][kl]);
-          ee[0] = ev.x;
-          ee[1] = ev.y;
-          ee[2] = ev.z;
-          ee[3] = ev.w;
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = rg * 4 + c;
-          float p = fast_exp2(fmaf(sacc[r], sl2, -l2));
-          if (partial) {
-            const int j = j0 + kl + c;
-            const bool live = j <= qi && qi < ee[c] && j < N;
-            p = live ? p : 0.f;
-          }
-          sf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - dii));
-        }
-      }
+      for (int r = 0; r < 16; ++r) sf[r >> 3][r & 7] = (__bf16)(pv[r] * (pacc[r] - dii));
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          dqa[db] = mfma32x32x16(tile_frag_t(Ks[buf], kk * 32 + 16 * ks, 32 * db, lane), sf[ks],
+          dqa[db] = mfma32x32x16(tile_frag_t(Ks[buf], lt, kk * 32 + 16 * ks, 32 * db), sf[ks],
                                  dqa[db]);
     }
   };
@@ -824,8 +408,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tn = it.next();
     if (tn >= 0) load_tile(tn);
     const int j0 = t * KT;
-    const bool full = (j0 + KT - 1 <= i0) && (eminb[t] >= i1) && (j0 + KT <= N);
-    compute(buf, j0, !full);
+    const int emn = __builtin_amdgcn_readfirstlane(eminb[t]);
+    body(buf, j0, !((j0 + KT - 1 <= i0) && (emn >= i1) && (j0 + KT <= N)));
     if (tn >= 0) store_tile(buf ^ 1);
     __syncthreads();
     buf ^= 1;
@@ -907,10 +491,10 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   st = ks_check_launch("ks_evict_attn_bwd(pre)");
   if (st != KS_OK) return st;
 
-  const int nkt = (N + KW8 - 1) / KW8;
+  const int nkt = (N + KW - 1) / KW;
   const long long nkv = static_cast<long long>(B) * Hkv * nkt;
   KS_REQUIRE(nkv < (1LL << 31), "ks_evict_attn_bwd: grid too large");
-  hipLaunchKernelGGL(dkdv_d128_kernel, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq, kk,
+  hipLaunchKernelGGL(dkdv_kernel, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq, kk,
                      vv, e, emin, emax, lse, di, gg, static_cast<bf16_t*>(dk),
                      static_cast<bf16_t*>(dv), B, N, Hq, Hkv, ntiles, scale);
   st = ks_check_launch("ks_evict_attn_bwd(dkdv)");
@@ -922,7 +506,7 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   const long long total_q = (real_q + 7) / 8 * 8;
   KS_REQUIRE(total_q < (1LL << 31), "ks_evict_attn_bwd: grid too large");
 #define KS_DQ_LAUNCH(HPW_)                                                                   \
-  hipLaunchKernelGGL((dq_d128_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(512), \
+  hipLaunchKernelGGL((dq_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(512), \
                      0, s, qq, kk, vv, e, emin, emax, lse, di, gg, static_cast<bf16_t*>(dq), B, \
                      N, Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
   if (hpw == 4) KS_DQ_LAUNCH(4);

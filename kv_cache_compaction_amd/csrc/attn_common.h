@@ -51,31 +51,33 @@ struct LiveTiles {
 };
 
 // ---------------------------------------------------------------------------
-// LDS tiles of 128-element bf16 rows (D = 128), stored in natural [row][d]
-// order with the 16-byte chunks of row r permuted by chunk ^ swz(r).  The
-// permutation makes both access patterns of the MFMA loops conflict-free:
-//   * 16-byte reads of one chunk from 16 consecutive rows (swz is a bijection
-//     on r mod 16), and
-//   * ds_read_b64_tr_b16 transpose reads, where a 16-lane group reads 4
-//     consecutive rows x 16 consecutive columns (swz moves the 4 rows to
-//     distinct 64-byte groups).
+// LDS tiles of 128-element bf16 rows (D = 128).  A staged row occupies 272
+// bytes (256 of data + 16 of padding), and within every block of 16 rows,
+// row 4a + b is stored at position 4b + a.  Both access patterns of the MFMA
+// loops are then free of bank conflicts:
+//   * 16-byte reads of one chunk from 16 consecutive rows (the rows land on
+//     16 distinct 16-byte bank groups because of the 16-byte padding), and
+//   * ds_read_b64_tr_b16 transpose reads, where 32 lanes read 4 consecutive
+//     rows x 32 consecutive columns (the permutation spreads the 4 rows 4
+//     positions apart, so row + chunk covers all 16 bank groups once),
+// and every operand address is a per-lane base plus a compile-time offset.
 // ---------------------------------------------------------------------------
-constexpr int kRowElems = 128;
+constexpr int kTileRow = 136;  // bf16 elements per staged row
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-// element offset of (row, col) in a swizzled tile
-__device__ __forceinline__ int tile_idx(int row, int col) {
-  return row * kRowElems + (((col >> 3) ^ swz(row)) << 3) + (col & 7);
-}
-
-// 16-byte chunk `chunk` of row `row`
-__device__ __forceinline__ bf16x8 tile_chunk(const bf16_t* t, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(t + row * kRowElems + ((chunk ^ swz(row)) << 3));
+__device__ __forceinline__ int tile_prow(int r) {
+  return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 __device__ __forceinline__ void tile_store_chunk(bf16_t* t, int row, int chunk, u32x4 v) {
-  *reinterpret_cast<u32x4*>(t + row * kRowElems + ((chunk ^ swz(row)) << 3)) = v;
+  *reinterpret_cast<u32x4*>(t + tile_prow(row) * kTileRow + chunk * 8) = v;
+}
+
+// per-lane base of operand reads that give lane l row (rbase + l % 32)
+__device__ __forceinline__ int tile_lane_a(int lane) { return tile_prow(lane & 31) * kTileRow; }
+
+// 16-byte chunk `chunk` of row rbase + lane % 32 (rbase a multiple of 16)
+__device__ __forceinline__ bf16x8 tile_chunk(const bf16_t* t, int lane_a, int rbase, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(t + lane_a + rbase * kTileRow + chunk * 8);
 }
 
 __device__ __forceinline__ bf16x4 lds_tr16(const bf16_t* p) {
@@ -83,19 +85,25 @@ __device__ __forceinline__ bf16x4 lds_tr16(const bf16_t* p) {
       (__attribute__((address_space(3))) bf16x4*)(p));
 }
 
+// per-lane base of the transpose reads below
+__device__ __forceinline__ int tile_lane_t(int lane) {
+  const int j = lane & 15, g = lane >> 4, h = lane >> 5;
+  return (4 * (j >> 2) + h) * kTileRow + 16 * (g & 1) + 4 * (j & 3);
+}
+
 // A operand of a 32x32x16 MFMA that contracts over tile ROWS: lane l gets
 // X[k(v)][dbase + l % 32] for v = 0..7 with
-//   k(v) = r0 + 8 * (v / 4) + 4 * (l / 32) + v % 4,
-// the k order in which a 32x32 accumulator holds its rows (so P^T / dS^T
-// taken straight from an S accumulator is the matching B operand).
-// ds_read_b64_tr_b16 semantics: within each 16-lane group, lane i receives
-// element i % 4 of the 8-byte reads of lanes 4r + i / 4, r = 0..3.
-__device__ __forceinline__ bf16x8 tile_frag_t(const bf16_t* t, int r0, int dbase, int lane) {
-  const int j = lane & 15, g = lane >> 4, h = lane >> 5;
-  const int row = r0 + 4 * h + (j >> 2);
-  const int col = dbase + 16 * (g & 1) + 4 * (j & 3);
-  const bf16x4 lo = lds_tr16(t + tile_idx(row, col));
-  const bf16x4 hi = lds_tr16(t + tile_idx(row + 8, col));
+//   k(v) = r0 + 8 * (v / 4) + 4 * (l / 32) + v % 4    (r0 a multiple of 16),
+// the k order in which a 32x32 accumulator holds its rows, so P^T or dS^T
+// taken straight from an S accumulator is the matching B operand.
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte reads of lanes 4r + i / 4 (r = 0..3); lane 4r + q
+// reads row k(r) (stored at position 4 q' ... see tile_prow) and columns
+// dbase + 16 (group % 2) + 4 q .. +3.
+__device__ __forceinline__ bf16x8 tile_frag_t(const bf16_t* t, int lane_t, int r0, int dbase) {
+  const bf16_t* p = t + lane_t + r0 * kTileRow + dbase;
+  const bf16x4 lo = lds_tr16(p);                 // v = 0..3: rows r0 + 4h + r
+  const bf16x4 hi = lds_tr16(p + 2 * kTileRow);  // v = 4..7: rows r0 + 8 + 4h + r
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 

@@ -434,8 +434,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int RS = 8 / HPW;   // 32-row subtiles per workgroup
   constexpr int BM = 32 * RS;   // query rows per workgroup
   constexpr int KT = kKeyTile;  // 64 keys per tile
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * kTileRow];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * kTileRow];
   __shared__ __attribute__((aligned(16))) int Es[2][KT];
 
   int lin = blockIdx.x;
@@ -455,6 +455,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int i1 = min(N, i0 + BM);
   const int lq = lane & 31, lh = lane >> 5;
   const int qi = wi0 + lq;  // this lane's query row
+  const int la = tile_lane_a(lane), lt = tile_lane_t(lane);
 
   const size_t tok = static_cast<size_t>(Hkv) * D;
   const bf16_t* kb = k + static_cast<size_t>(b) * N * tok + static_cast<size_t>(hkv) * D;
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (tid < KT) Es[buf][tid] = er;
   };
 
-  auto compute = [&](int buf, int j0, bool partial) {
+  auto compute = [&](int buf, int j0, bool partial) {  // partial: uniform
     f32x16 sacc[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) sacc[kk][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        sacc[kk] = mfma32x32x16(tile_chunk(Ks[buf], kk * 32 + lq, 2 * s + lh), qf[s], sacc[kk]);
+        sacc[kk] = mfma32x32x16(tile_chunk(Ks[buf], la, kk * 32, 2 * s + lh), qf[s], sacc[kk]);
     }
     if (partial) {
 #pragma unroll
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        oacc[db] = mfma32x32x16(tile_frag_t(Vs[buf], kk * 16, db * 32, lane), pf[kk], oacc[db]);
+        oacc[db] = mfma32x32x16(tile_frag_t(Vs[buf], lt, kk * 16, db * 32), pf[kk], oacc[db]);
   };
 
   LiveTiles it;
@@ -581,17 +582,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tn = it.next();
     if (tn >= 0) load_tile(tn);
     const int j0 = t * KT;
-    const bool full = (j0 + KT - 1 <= i0) && (eminb[t] >= i1) && (j0 + KT <= N);
-    compute(buf, j0, !full);
+    const int emn = __builtin_amdgcn_readfirstlane(eminb[t]);
+    compute(buf, j0, !((j0 + KT - 1 <= i0) && (emn >= i1) && (j0 + KT <= N)));
     if (tn >= 0) store_tile(buf ^ 1);
     __syncthreads();
     buf ^= 1;
     t = tn;
   }
 
-  const float lt = lrow + __shfl_xor(lrow, 32);
+  const float ltot = lrow + __shfl_xor(lrow, 32);
   if (qi < N) {
-    const float inv = 1.f / lt;
+    const float inv = 1.f / ltot;
     bf16_t* op = o + (static_cast<size_t>(b) * N + qi) * Hq * D + static_cast<size_t>(hq) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                   pack_bf16x2(oacc[db][rg * 4 + 2] * inv, oacc[db][rg * 4 + 3] * inv)};
       }
     if (lse && lh == 0)
-      lse[(static_cast<size_t>(b) * Hq + hq) * N + qi] = (mrow + __log2f(lt)) * KS_LN2;
+      lse[(static_cast<size_t>(b) * Hq + hq) * N + qi] = (mrow + __log2f(ltot)) * KS_LN2;
   }
 }
 
