@@ -194,6 +194,29 @@ ks_status ks_paged_decode(const void* q, const void* k_pool,
                           int num_pool_blocks, int dtype, float scale,
                           void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * ks_append_kv -- write the newly generated token of every sequence into its
+ * paged cache: the key rotated at its LOGICAL position, and the value.
+ *
+ * Keys are stored already rotated, so compaction can move or splice blocks
+ * without touching them, and the next token continues the original position
+ * count (explainer, RoPE paragraph).  The token goes to slot
+ * s = seq_lens[b] - 1, i.e. block table[b][s / 16], row s % 16.
+ *
+ * k_new, v_new  [B, Hkv, D] bf16 (k_new unrotated; neither is modified)
+ * pos           int32 [B]   logical position of the new token
+ * table         int32 [B, max_blocks], seq_lens int32 [B] (already counting
+ *               the new token; sequences with seq_lens[b] < 1 are skipped)
+ * k_pool, v_pool [num_pool_blocks, Hkv, 16, D] bf16, written in place;
+ *               a table entry outside [0, num_pool_blocks) skips that
+ *               sequence (nothing outside the pool is written)
+ * dtype KS_BF16, D = 128; RoPE base as in ks_rope_logical.
+ */
+ks_status ks_append_kv(const void* k_new, const void* v_new, const int32_t* pos,
+                       const int32_t* table, const int32_t* seq_lens, void* k_pool,
+                       void* v_pool, int B, int Hkv, int D, int max_blocks,
+                       int num_pool_blocks, int dtype, float base, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,7 @@ _SIGS = {
     "ks_compact_block_table": ([_vp] * 7 + [_i, _i, _vp], _i),
     "ks_paged_decode_workspace": ([_i, _i, _i, _i], _sz),
     "ks_paged_decode": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+    "ks_append_kv": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _f, _vp], _i),
 }
 
 _lib = None
@@ -250,3 +251,28 @@ def ks_paged_decode(q, k_pool, v_pool, table, seq_lens, scale=None, out=None, ls
                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("ks_paged_decode", st)
     return out, lse
+
+
+def ks_append_kv(k_new, v_new, pos, table, seq_lens, k_pool, v_pool, base=10000.0,
+                 stream=None):
+    """Rotate k_new [B, Hkv, D] at pos [B] and write it and v_new into pool
+    slot seq_lens[b] - 1 of every sequence (in place on the pools)."""
+    lib = load_library()
+    B, Hkv, D = k_new.shape
+    NB = k_pool.shape[0]
+    _cuda_contig("k_new", k_new)
+    _cuda_contig("v_new", v_new, k_new.dtype)
+    _cuda_contig("k_pool", k_pool, k_new.dtype)
+    _cuda_contig("v_pool", v_pool, k_new.dtype)
+    _cuda_contig("pos", pos, torch.int32)
+    _cuda_contig("table", table, torch.int32)
+    _cuda_contig("seq_lens", seq_lens, torch.int32)
+    _need(tuple(v_new.shape) == (B, Hkv, D), "v_new shape")
+    _need(tuple(k_pool.shape) == (NB, Hkv, KS_BLOCK, D) and v_pool.shape == k_pool.shape,
+          "pool shape")
+    _need(tuple(pos.shape) == (B,) and tuple(seq_lens.shape) == (B,) and table.shape[0] == B,
+          "pos/seq_lens/table shape")
+    st = lib.ks_append_kv(_ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(table), _ptr(seq_lens),
+                          _ptr(k_pool), _ptr(v_pool), B, Hkv, D, table.shape[1], NB,
+                          _dtype_code(k_new), float(base), _stream(stream))
+    _check("ks_append_kv", st)

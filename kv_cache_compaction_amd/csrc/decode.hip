@@ -221,6 +221,56 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   if (lse && d == 0) lse[static_cast<size_t>(b) * Hq + h] = (M + __log2f(den)) * KS_LN2;
 }
 
+// ---------------------------------------------------------------------------
+// append: rotate the new token's key at its logical position and write key
+// and value into pool slot seq_len - 1 (block table entry (seq_len - 1) / 16).
+// Keys are stored already rotated, so later compaction can move blocks
+// without touching their contents (explainer, RoPE paragraph).  One
+// workgroup per sequence; angles in fp64 as in ks_rope_logical.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void append_kernel(
+    const bf16_t* __restrict__ k_new, const bf16_t* __restrict__ v_new,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ seq_lens, bf16_t* __restrict__ kpool,
+    bf16_t* __restrict__ vpool, int Hkv, int MB, int NB, double log2_base) {
+  __shared__ float2 cs[D / 2];
+  const int b = blockIdx.x;
+  const int L = min(seq_lens[b], 16 * MB);
+  if (L < 1) return;
+  const int slot = L - 1;
+  const int pid = table[static_cast<size_t>(b) * MB + (slot >> 4)];
+  if (static_cast<unsigned>(pid) >= static_cast<unsigned>(NB)) return;
+  for (int kk = threadIdx.x; kk < D / 2; kk += blockDim.x) {
+    const double inv_freq = exp2(-2.0 * kk / D * log2_base);
+    double sn, c;
+    sincos(static_cast<double>(pos[b]) * inv_freq, &sn, &c);
+    cs[kk] = make_float2(static_cast<float>(c), static_cast<float>(sn));
+  }
+  __syncthreads();
+  // thread = (head, 8-element chunk of the first half)
+  for (int idx = threadIdx.x; idx < Hkv * (D / 16); idx += blockDim.x) {
+    const int h = idx / (D / 16), ch = idx % (D / 16);
+    const size_t src = (static_cast<size_t>(b) * Hkv + h) * D + ch * 8;
+    const size_t dst = ((static_cast<size_t>(pid) * Hkv + h) * 16 + (slot & 15)) * D + ch * 8;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(k_new + src);
+    const u32x4 bb = *reinterpret_cast<const u32x4*>(k_new + src + D / 2);
+    u32x4 ra, rb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float2 c0 = cs[ch * 8 + 2 * i], c1 = cs[ch * 8 + 2 * i + 1];
+      const float x0 = lo_bf16(a[i]), x1 = hi_bf16(a[i]);
+      const float y0 = lo_bf16(bb[i]), y1 = hi_bf16(bb[i]);
+      ra[i] = pack_bf16x2(x0 * c0.x - y0 * c0.y, x1 * c1.x - y1 * c1.y);
+      rb[i] = pack_bf16x2(y0 * c0.x + x0 * c0.y, y1 * c1.x + x1 * c1.y);
+    }
+    *reinterpret_cast<u32x4*>(kpool + dst) = ra;
+    *reinterpret_cast<u32x4*>(kpool + dst + D / 2) = rb;
+    *reinterpret_cast<u32x4*>(vpool + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+    *reinterpret_cast<u32x4*>(vpool + dst + D / 2) =
+        *reinterpret_cast<const u32x4*>(v_new + src + D / 2);
+  }
+}
+
 inline int nsplit_for(int max_blocks) { return (max_blocks + kSplit - 1) / kSplit; }
 
 }  // namespace
@@ -280,4 +330,27 @@ extern "C" ks_status ks_paged_decode(const void* q, const void* k_pool, const vo
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(Hq, B), dim3(D), 0, s, part_o, part_ml, seq_lens,
                      static_cast<bf16_t*>(out), lse, Hq, max_blocks, nsplit);
   return ks_check_launch("ks_paged_decode(reduce)");
+}
+
+extern "C" ks_status ks_append_kv(const void* k_new, const void* v_new, const int32_t* pos,
+                                  const int32_t* table, const int32_t* seq_lens, void* k_pool,
+                                  void* v_pool, int B, int Hkv, int Dh, int max_blocks,
+                                  int num_pool_blocks, int dtype, float base, void* stream) {
+  KS_REQUIRE(B >= 0 && Hkv > 0 && max_blocks >= 0 && num_pool_blocks >= 0,
+             "ks_append_kv: bad sizes");
+  KS_REQUIRE(base > 1.0f, "ks_append_kv: base must be > 1");
+  if (dtype != KS_BF16 || Dh != D)
+    return ks_fail(KS_ERR_UNSUPPORTED, "ks_append_kv: only bf16 with D=128 (dtype=%d D=%d)",
+                   dtype, Dh);
+  if (B == 0 || max_blocks == 0) return KS_OK;
+  KS_REQUIRE(k_new && v_new && pos && table && seq_lens && k_pool && v_pool,
+             "ks_append_kv: null pointer");
+  KS_REQUIRE(ks_aligned16(k_new) && ks_aligned16(v_new) && ks_aligned16(k_pool) &&
+                 ks_aligned16(v_pool),
+             "ks_append_kv: tensors must be 16-byte aligned");
+  hipLaunchKernelGGL(append_kernel, dim3(B), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new), pos,
+                     table, seq_lens, static_cast<bf16_t*>(k_pool), static_cast<bf16_t*>(v_pool),
+                     Hkv, max_blocks, num_pool_blocks, log2(static_cast<double>(base)));
+  return ks_check_launch("ks_append_kv");
 }

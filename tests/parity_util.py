@@ -8,9 +8,17 @@ import torch
 # (fp32 accumulation), <= 1e-5 for the fp32 path.  Because bf16 outputs of the
 # N(0,1)*0.5 workloads are only ~1e-3..1e-1 in magnitude, the bf16 gate also
 # bounds the error relative to the output's scale (max and L2).
-ATOL = {"bf16": 2e-2, "f32": 1e-5}
-REL_MAX = {"bf16": 1.5e-2, "f32": 1e-5}
-REL_L2 = {"bf16": 1e-2, "f32": 1e-6}
+#
+# Gradients ("bf16grad") get a looser normalised-max bound.  The backward
+# uses D_i = rowsum(dO o O) with O the bf16 output of the forward, so each
+# row carries an error of about 2^-9 |dO| |O| in D_i.  On a row whose dQ is
+# small against its inputs (e.g. a row that sees two keys whose values nearly
+# cancel along dO) this is a few percent of that row's dQ, although the
+# absolute error stays ~1e-3.  Rows with many live keys sit at the bf16
+# rounding floor (~0.25% relative), which the L2 bound still enforces.
+ATOL = {"bf16": 2e-2, "bf16grad": 2e-2, "f32": 1e-5}
+REL_MAX = {"bf16": 1.5e-2, "bf16grad": 5e-2, "f32": 1e-5}
+REL_L2 = {"bf16": 1e-2, "bf16grad": 1e-2, "f32": 1e-6}
 
 
 def announce(msg):
@@ -26,7 +34,7 @@ def f64(t):
 # below this output scale the relative metrics are meaningless (an exactly
 # zero reference, e.g. dQ of a row that sees a single key); the absolute
 # bound still applies there
-SCALE_FLOOR = {"bf16": 1e-4, "f32": 1e-6}
+SCALE_FLOOR = {"bf16": 1e-4, "bf16grad": 1e-4, "f32": 1e-6}
 
 
 def errors(actual, ref, kind="bf16"):

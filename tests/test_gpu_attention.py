@@ -102,7 +102,7 @@ def test_cfg2_forward(cfg2):
 
 def test_cfg2_backward(cfg2):
     for name, got, ref in zip(("dQ", "dK", "dV"), cfg2["got"][2:], cfg2["ref"][2:]):
-        gate(got, ref, "bf16", name)
+        gate(got, ref, "bf16grad", name)
 
 
 def test_cfg2_negative_controls(cfg2):
@@ -149,9 +149,9 @@ def test_bf16_backward_random_masks(N, Hq, Hkv, seed):
     dq, dk, dv = ks.ks_evict_attn_bwd(qg, kg, vg, eg, o, lse, dog)
     torch.cuda.synchronize()
     rdq, rdk, rdv = O.attn_bwd(f64(q), f64(k), f64(v), e, f64(do))
-    gate(dq, rdq, "bf16", "dQ")
-    gate(dk, rdk, "bf16", "dK")
-    gate(dv, rdv, "bf16", "dV")
+    gate(dq, rdq, "bf16grad", "dQ")
+    gate(dk, rdk, "bf16grad", "dK")
+    gate(dv, rdv, "bf16grad", "dV")
 
 
 def test_bf16_diagonal_only_and_causal():

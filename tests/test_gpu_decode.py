@@ -141,3 +141,27 @@ def test_invalid_block_id_gives_nan_not_fault():
     torch.cuda.synchronize()
     assert torch.isfinite(out[0].float()).all()
     assert torch.isnan(out[1].float()).all()
+
+
+def test_append_kv_rotates_and_places():
+    lens = np.array([1, 16, 17, 40, 0], np.int32)      # lengths counting the new token
+    B, Hkv, D = len(lens), 4, 128
+    _, kp, vp, table = _direct(B, 8, Hkv, lens, 99)
+    k0, v0 = kp.clone(), vp.clone()
+    k_new = normal_tensor((B, Hkv, D), 101, 0.5, torch.bfloat16, DEV)
+    v_new = normal_tensor((B, Hkv, D), 102, 0.5, torch.bfloat16, DEV)
+    pos = np.array([0, 17, 4096, 65791, 5], np.int32)
+    ks.ks_append_kv(k_new, v_new, _gpu(pos), _gpu(table), _gpu(lens), kp, vp)
+    torch.cuda.synchronize()
+    ref = O.rope(f64(k_new)[:, None], pos[:, None])[:, 0]       # [B, Hkv, D]
+    touched = torch.zeros(kp.shape[:3], dtype=torch.bool, device=DEV)
+    for b in range(B):
+        if lens[b] < 1:
+            continue
+        s = int(lens[b]) - 1
+        p = int(table[b, s // 16])
+        got = f64(kp[p, :, s % 16])
+        assert np.all(np.abs(got - ref[b]) <= np.abs(ref[b]) * 2.0**-8 + 1e-6), b
+        assert torch.equal(vp[p, :, s % 16], v_new[b])
+        touched[p, :, s % 16] = True
+    assert torch.equal(kp[~touched], k0[~touched]) and torch.equal(vp[~touched], v0[~touched])

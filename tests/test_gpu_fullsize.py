@@ -58,9 +58,12 @@ def run_training_config(cfg, b, hkv, key_blocks):
     sdo = do.float().sum(1).view(B, Hkv, G, D).sum(2)
     assert torch.allclose(sdv, sdo, atol=0.05 * sdo.abs().max().item()), \
         (sdv - sdo).abs().max().item()
-    lhs = (q.float() * dq.float()).sum().item()
-    rhs = (k.float() * dk.float()).sum().item()
-    assert abs(lhs - rhs) <= 0.02 * max(abs(lhs), abs(rhs)) + 1e-3, (lhs, rhs)
+    a, c = q.float() * dq.float(), k.float() * dk.float()
+    lhs, rhs = a.sum().item(), c.sum().item()
+    # the exact sums are equal; bf16 rounding of each dq, dk element (2^-9
+    # relative) moves them by about 2^-9 * sqrt(sum of squared terms)
+    noise = 2.0**-9 * (a.square().sum().sqrt().item() + c.square().sum().sqrt().item())
+    assert abs(lhs - rhs) <= 8 * noise, (lhs, rhs, noise)
 
     tr = traces[b]
     rows = _sample_rows(tr, np.random.default_rng(5))
@@ -72,11 +75,11 @@ def run_training_config(cfg, b, hkv, key_blocks):
         gate(o[b, rows, hkv * G + hh], ro, "bf16", f"O rows h{hh}")
         gate(lse[b, hkv * G + hh, rows], rl, "bf16", f"LSE rows h{hh}")
         rdq = O.attn_bwd_rows(qs, kk, v_h, eb, do_h, 0, hh, rows)
-        gate(dq[b, rows, hkv * G + hh], rdq, "bf16", f"dQ rows h{hh}")
+        gate(dq[b, rows, hkv * G + hh], rdq, "bf16grad", f"dQ rows h{hh}")
     for keys in key_blocks(tr):
         rdk, rdv = O.attn_bwd_keys(qs, kk, v_h, eb, do_h, 0, 0, keys)
-        gate(dk[b, keys, hkv], rdk, "bf16", f"dK keys {keys[0]}..")
-        gate(dv[b, keys, hkv], rdv, "bf16", f"dV keys {keys[0]}..")
+        gate(dk[b, keys, hkv], rdk, "bf16grad", f"dK keys {keys[0]}..")
+        gate(dv[b, keys, hkv], rdv, "bf16grad", f"dV keys {keys[0]}..")
 
 
 def test_cfg3_summary_32k_sampled():

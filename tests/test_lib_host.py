@@ -94,3 +94,12 @@ def test_decode_and_rope_argument_checks(lib):
 def test_python_binding_error_type():
     err = _lib.KSError("ks_x", 4, "workspace 1 < 2 bytes")
     assert "WORKSPACE_TOO_SMALL" in str(err) and err.status == 4
+
+
+def test_append_argument_checks(lib):
+    st, _ = _status(lib, "ks_append_kv", *([FAKE] * 7), 2, 8, 64, 10, 100, 1, 10000.0, None)
+    assert st == 2  # D = 64 not provided
+    st, _ = _status(lib, "ks_append_kv", *([FAKE] * 7), 2, 8, 128, 10, 100, 1, 0.5, None)
+    assert st == 1  # base must exceed 1
+    st, _ = _status(lib, "ks_append_kv", *([FAKE] * 7), 0, 8, 128, 10, 100, 1, 10000.0, None)
+    assert st == 0  # nothing to do

@@ -7,7 +7,7 @@ no attention, no table compaction); the oracle and the HIP library each
 implement those on their own.
 """
 from .traces import (  # noqa: F401
-    KS_NEVER, BLOCK, Trace, build_trace, check_trace, DecodeBatch,
+    KS_NEVER, BLOCK, Trace, build_trace, check_trace, DecodeBatch, evict_units,
     build_decode_batch, normal_tensor, trace_blocks_keep,
 )
 from .configs import CONFIGS, Config, config_trace_batch, stacked_e  # noqa: F401

@@ -51,6 +51,9 @@ class Trace:
     events: list                     # sorted event indices
     evicted: dict                    # event index -> [(a, b)] evicted spans
     e: np.ndarray = field(repr=False)  # int32 [N]
+    live_units: list = field(default_factory=list)  # live spans after the trace
+    overlap: int = 0
+    summary: int = 0
 
 
 def build_trace(rng: np.random.Generator, N: int, P: int, budget: int,
@@ -95,32 +98,45 @@ def build_trace(rng: np.random.Generator, N: int, P: int, budget: int,
         if live + nxt <= budget:
             continue
         t_ev = b
-        out = []
-        if strategy in ("recent", "window"):
-            first = 0 if (strategy == "window" or P == 0) else 1
-            target = budget // 2
-            while live > target and len(units) > first + 1:
-                u = units.pop(first)
-                out.append(u)
-                live -= u[1] - u[0]
-        else:
-            keep_lo = t_ev - (overlap + summary)
-            kept = [units[0]] if P > 0 else []
-            for (x, y) in (units[1:] if P > 0 else units):
-                if y <= keep_lo:
-                    out.append((x, y))
-                elif x >= keep_lo:
-                    kept.append((x, y))
-                else:
-                    out.append((x, keep_lo))
-                    kept.append((keep_lo, y))
-            units = kept
+        units, out = evict_units(units, t_ev, strategy, budget, P, overlap, summary)
         for (x, y) in out:
             e[x:y] = t_ev
         events.append(t_ev)
         evicted[t_ev] = out
     return Trace(N=N, P=P, budget=budget, strategy=strategy, turns=turns,
-                 events=events, evicted=evicted, e=e.astype(np.int32))
+                 events=events, evicted=evicted, e=e.astype(np.int32),
+                 live_units=list(units), overlap=overlap, summary=summary)
+
+
+def evict_units(units, t_ev, strategy, budget, P, overlap=0, summary=0):
+    """Apply one compaction event at trace index ``t_ev`` to the live spans
+    ``units`` (oldest first; the prompt, if any, is ``units[0]``).
+
+    Returns ``(kept_units, evicted_spans)`` following the strategy rules of
+    ``build_trace``.
+    """
+    units = list(units)
+    live = sum(y - x for x, y in units)
+    out = []
+    if strategy in ("recent", "window"):
+        first = 0 if (strategy == "window" or P == 0) else 1
+        target = budget // 2
+        while live > target and len(units) > first + 1:
+            u = units.pop(first)
+            out.append(u)
+            live -= u[1] - u[0]
+        return units, out
+    keep_lo = t_ev - (overlap + summary)
+    kept = [units[0]] if P > 0 else []
+    for (x, y) in (units[1:] if P > 0 else units):
+        if y <= keep_lo:
+            out.append((x, y))
+        elif x >= keep_lo:
+            kept.append((x, y))
+        else:
+            out.append((x, keep_lo))
+            kept.append((keep_lo, y))
+    return kept, out
 
 
 def check_trace(tr: Trace) -> None:
