@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (a known-size "
+                         "reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -130,7 +133,10 @@ def main():
     kp = normal_tensor((NB, H4kv, 16, D), 4001, 0.5, bf, dev)
     vp = normal_tensor((NB, H4kv, 16, D), 4002, 0.5, bf, dev)
     q4 = normal_tensor((DB, 1, H4q, D), 4003, 0.5, bf, dev)
+    k4 = normal_tensor((DB, H4kv, D), 4004, 0.5, bf, dev)
+    v4 = normal_tensor((DB, H4kv, D), 4005, 0.5, bf, dev)
     pos4 = torch.from_numpy(db.pos[:, None].astype(np.int32)).to(dev)
+    pos4f = pos4[:, 0].contiguous()
     table0 = torch.from_numpy(db.table0).to(dev)
     nblk0 = torch.from_numpy(db.nblk0).to(dev)
     keeps = [torch.from_numpy(db.keeps[r]).to(dev) for r in range(db.keeps.shape[0])]
@@ -142,8 +148,12 @@ def main():
     ws_d = torch.empty(ks.ks_paged_decode_workspace(DB, H4q, D, MB), dtype=torch.uint8,
                        device=dev)
     L = db.live_len.astype(np.int64) + 1
+    # decode step bytes: K/V of every live token once, q (rotated in place:
+    # read + write), the appended token's k/v (read + write), output, lse,
+    # table entries and lengths
     dec_bytes = int((L * H4kv * D * 2 * 2).sum()) + 2 * DB * H4q * D * 2 + \
-        int(((L + 15) // 16).sum()) * 4 + DB * 4 + DB * H4q * 4
+        2 * 2 * DB * H4kv * D * 2 + DB * H4q * D * 2 + DB * H4q * 4 + \
+        int(((L + 15) // 16).sum()) * 4 + DB * 4
     comp_bytes = 0
     nb_cur = db.nblk0.astype(np.int64).copy()
     for r in range(db.keeps.shape[0]):
@@ -178,12 +188,22 @@ def main():
         t1(ev, "compact")
         ev = t0()
         ks.ks_rope_logical(q4, None, pos4, stream=stream)
+        ks.ks_append_kv(k4, v4, pos4f, src, seq_lens, kp, vp, stream=stream)
         ks.ks_paged_decode(q4[:, 0], kp, vp, src, seq_lens, out=out4, lse=lse4, ws=ws_d,
                            stream=stream)
         t1(ev, "decode")
 
     # q4[:, 0] is a view of a contiguous [B, 1, Hq, D] tensor: contiguous as [B, Hq, D]
     assert q4[:, 0].is_contiguous()
+
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src_c = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst_c = torch.empty_like(src_c)
+        torch.cuda.synchronize()
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
 
     for _ in range(args.warmup):
         step()

@@ -147,9 +147,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int srow = tid >> 4, sc = tid & 15;
   u32x4 xq, xo;
   float lr = 0.f;
+  // chunk order: query chunks walked backwards from the end of the range,
+  // heads innermost.  Key tiles evicted by the same event share that end, so
+  // workgroups running side by side read the same Q/dO chunks at about the
+  // same time and share them through L2.
+  auto chunk_row = [&](int idx) { return (c_end - 1 - idx / G) * BQ; };
   auto load_chunk = [&](int idx) {
-    const int h = hkv * G + idx / nc;
-    const int c0 = (c_begin + idx % nc) * BQ;
+    const int h = hkv * G + idx % G;
+    const int c0 = chunk_row(idx);
     const int row = c0 + srow;
     const size_t off = (static_cast<size_t>(b) * N + row) * tokq + static_cast<size_t>(h) * D +
                        sc * 8;
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int idx = 0; idx < nchunks; ++idx) {
     const bool more = idx + 1 < nchunks;
     if (more) load_chunk(idx + 1);
-    compute(buf, (c_begin + idx % nc) * BQ);
+    compute(buf, chunk_row(idx));
     if (more) store_chunk(buf ^ 1);
     __syncthreads();
     buf ^= 1;
