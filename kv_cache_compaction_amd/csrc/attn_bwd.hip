@@ -31,13 +31,14 @@ constexpr int KW = 256;        // keys per dK/dV workgroup (8 waves x 32)
 constexpr int KT = kKeyTile;   // keys per dQ tile
 
 // ---------------------------------------------------------------------------
-// D_i = sum_d dO_id O_id  (fp32), and LSE in log2 units
+// D_i = sum_d dO_id O_id (fp32) and LSE in log2 units, both laid out
+// [B][Hq][Npad] with Npad = N rounded up to BQ; padding rows hold 0 so that
+// whole 32-row chunks can be staged without bounds checks.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ o,
-                                                      const bf16_t* __restrict__ dout,
-                                                      float* __restrict__ di, long long rows,
-                                                      int N, int Hq) {
-  // 16 threads per (b, i, h) row of D = 128 values
+__global__ __launch_bounds__(256) void bwd_pre_kernel(
+    const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ di, float* __restrict__ lse2, long long rows, int N, int Npad, int Hq) {
+  // 16 threads per (b, i, h) row of D = 128 values; rows past B*N*Hq are padding
   const long long r = static_cast<long long>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
   float acc = 0.f;
@@ -50,48 +51,156 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__
   }
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (r < rows && c == 0) {
-    // r = (b * N + i) * Hq + h  ->  di[(b * Hq + h) * N + i]
+  if (c != 0) return;
+  if (r < rows) {
+    // r = (b * N + i) * Hq + h  ->  [(b * Hq + h) * Npad + i]
     const long long h = r % Hq;
     const long long bi = r / Hq;
     const long long b = bi / N, i = bi % N;
-    di[(b * Hq + h) * N + i] = acc;
+    const long long bh = b * Hq + h;
+    di[bh * Npad + i] = acc;
+    lse2[bh * Npad + i] = lse[bh * N + i] * KS_LOG2E;
+  } else if (Npad > N) {
+    const long long pr = r - rows;  // padding entry pr of (Npad - N) per (b, h)
+    const long long bh = pr / (Npad - N), i = N + pr % (Npad - N);
+    di[bh * Npad + i] = 0.f;
+    lse2[bh * Npad + i] = 0.f;
   }
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV.  K stays in registers as the B operand of S = Q K^T; V of the 256
 // keys stays in LDS for the whole walk (B operand of dP = dO V^T).  Query
-// chunks are staged once per workgroup; dO^T and Q^T come from transpose
+// chunks (Q, dO, LSE, D_i of 32 rows of one head) go from global memory
+// straight into LDS with LDS-DMA loads (global_load_lds_dwordx4, no
+// registers), NBUF chunks in flight, so a chunk's loads are issued NBUF - 1
+// chunk computations before it is used.  dO^T and Q^T come from transpose
 // reads.  Workgroups are ordered key-tile major so the heavy prompt tiles
 // (whose queries run to the end of the trace) start first.
+//
+// A staged chunk is a Q tile followed by a dO tile, each 32 rows of 17
+// 16-byte slots (see attn_common.h): 1088 slots, 17 wave-wide DMA
+// instructions.  Wave w fills slots [64 w, 64 w + 64) and [64 (w + 8), ...),
+// and every wave fills the last 64 slots [1024, 1088) with the same bytes:
+// each wave then issues the same 3 unconditional DMA loads per chunk, which
+// keeps the per-wave load count, and the waits built on it, exact.  The pad
+// slot of tile position p < 8 carries LSE (Q tile) or D_i (dO tile) of rows
+// 4p .. 4p + 3; the other pad slots receive a harmless copy of the same.
 // ---------------------------------------------------------------------------
+constexpr int NBUF = 4;                       // staged chunks
+constexpr int TSLOTS = BQ * (kTileRow / 8);   // 16-byte slots per 32-row tile
+constexpr int CELEMS = 2 * BQ * kTileRow;     // bf16 elements per staged chunk
+constexpr int DMA_PER_WAVE = 3;
+
+__device__ __forceinline__ void lds_dma16(const void* src, bf16_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_dst), 16,
+                                   0, 0);
+}
+
+// wait until at most N vector-memory operations of this wave are pending
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
+  // (15 = no wait), vmcnt[5:4] in bits 15:14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// workgroup barrier without a memory fence: callers order their LDS-DMA
+// loads with wait_vm first; the empty asm statements keep the compiler from
+// moving memory accesses across it
+__device__ __forceinline__ void bar_nofence() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// packed description of one DMA slot: bit 0..1 kind (0 Q data, 1 dO data,
+// 2 LSE, 3 D_i), bits 2..6 row (data) or 4-row group (LSE, D_i), bits 7..10
+// 16-byte chunk of the row
+__device__ __forceinline__ int dma_slot_desc(int s) {
+  const int tile = s >= TSLOTS ? 1 : 0;
+  const int s2 = s - tile * TSLOTS;
+  const int p = s2 / 17, c = s2 - 17 * p;
+  if (c < 16) return tile | (tile_prow(p) << 2) | (c << 7);
+  return (2 + tile) | ((p & 7) << 2);
+}
+
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
-    const int32_t* __restrict__ emax, const float* __restrict__ lse,
+    const int32_t* __restrict__ emax, const float* __restrict__ lse2,
     const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk,
-    bf16_t* __restrict__ dv, int B, int N, int Hq, int Hkv, int ntiles, float scale) {
+    bf16_t* __restrict__ dv, int B, int N, int Npad, int Hq, int Hkv, int ntiles, float scale) {
   __shared__ __attribute__((aligned(16))) bf16_t Vst[KW * kTileRow];
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * kTileRow];
-  __shared__ __attribute__((aligned(16))) bf16_t Os[2][BQ * kTileRow];
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
-
+  __shared__ __attribute__((aligned(16))) bf16_t C0[CELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_t C1[CELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_t C2[CELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_t C3[CELEMS];
   const int nbh = B * Hkv;
   const int kt = blockIdx.x / nbh;
   const int bh = blockIdx.x % nbh;
   const int b = bh / Hkv, hkv = bh % Hkv;
   const int G = Hq / Hkv;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, lh = lane >> 5;
   const int la = tile_lane_a(lane), lt = tile_lane_t(lane);
   const int j0 = kt * KW;
   const int kw0 = j0 + 32 * w;
   const int jl = kw0 + lq;
   const size_t tokkv = static_cast<size_t>(Hkv) * D;
-  const size_t tokq = static_cast<size_t>(Hq) * D;
+  const int tokq = Hq * D;
   const float sl2 = scale * KS_LOG2E;
+
+  int emx = static_cast<int>(0x80000000), emn = 0x7fffffff;
+  {
+    const int t0 = j0 / kKeyTile;
+    const int t1 = min(ntiles - 1, t0 + KW / kKeyTile - 1);
+    for (int t = t0; t <= t1; ++t) {
+      emx = max(emx, emax[static_cast<size_t>(b) * ntiles + t]);
+      emn = min(emn, emin[static_cast<size_t>(b) * ntiles + t]);
+    }
+  }
+  // workgroup bounds, made provably uniform for the compiler
+  emx = __builtin_amdgcn_readfirstlane(emx);
+  emn = __builtin_amdgcn_readfirstlane(emn);
+  const int qend = min(N, emx);
+  const int c_begin = j0 / BQ;
+  const int c_end = (qend + BQ - 1) / BQ;
+  const int nc = c_end > c_begin ? c_end - c_begin : 0;
+  const int nchunks = nc * G;
+
+  // chunk order: query chunks walked backwards from the end of the range,
+  // heads innermost
+  auto chunk_row = [&](int idx) { return (c_end - 1 - idx / G) * BQ; };
+  const int dsc0 = dma_slot_desc(64 * w + lane);
+  const int dsc1 = dma_slot_desc(64 * (w + 8) + lane);
+  const int dsc2 = dma_slot_desc(1024 + lane);
+  // stage chunk min(idx, nchunks - 1) into buffer dst (the tail re-stages the
+  // last chunk, so every wave issues the same number of DMA loads per step)
+  auto issue = [&](bf16_t* dst, int idx) {
+    idx = min(idx, nchunks - 1);
+    const int h = hkv * G + idx % G;
+    const int c0 = chunk_row(idx);
+    const int lim = N - 1 - c0;  // rows past the end re-read row N - 1
+    const size_t rowq = (static_cast<size_t>(b) * N + c0) * tokq + static_cast<size_t>(h) * D;
+    const size_t rowl = (static_cast<size_t>(b) * Hq + h) * Npad + c0;
+    auto src = [&](int d) -> const void* {
+      const int kind = d & 3, r = (d >> 2) & 31, c = d >> 7;
+      if (kind < 2)
+        return (kind ? dout : q) + rowq + (min(r, lim) * tokq + c * 8);
+      return (kind == 3 ? di : lse2) + rowl + 4 * r;
+    };
+    lds_dma16(src(dsc0), dst + 64 * w * 8);
+    lds_dma16(src(dsc1), dst + 64 * (w + 8) * 8);
+    lds_dma16(src(dsc2), dst + 1024 * 8);
+  };
+  if (nchunks > 0) {
+    issue(C0, 0);
+    issue(C1, 1);
+    issue(C2, 2);
+  }
 
   bf16x8 kf[NSTEP];
   {
@@ -114,18 +223,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                           : u32x4{0u, 0u, 0u, 0u};
     tile_store_chunk(Vst, row, c, x);
   }
-
-  const int t0 = j0 / kKeyTile;
-  const int t1 = min(ntiles - 1, t0 + KW / kKeyTile - 1);
-  int emx = static_cast<int>(0x80000000), emn = 0x7fffffff;
-  for (int t = t0; t <= t1; ++t) {
-    emx = max(emx, emax[static_cast<size_t>(b) * ntiles + t]);
-    emn = min(emn, emin[static_cast<size_t>(b) * ntiles + t]);
-  }
-  // workgroup / wave bounds, made provably uniform for the compiler
-  emx = __builtin_amdgcn_readfirstlane(emx);
-  emn = __builtin_amdgcn_readfirstlane(emn);
-  const int qend = min(N, emx);
   int wemx = jl < N ? ej : static_cast<int>(0x80000000);
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) wemx = max(wemx, __shfl_xor(wemx, off));
@@ -138,66 +235,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) dka[db][r] = dva[db][r] = 0.f;
 
-  const int c_begin = j0 / BQ;
-  const int c_end = (qend + BQ - 1) / BQ;
-  const int nc = c_end > c_begin ? c_end - c_begin : 0;
-  const int nchunks = nc * G;
-
-  // staging: thread t copies chunk (t & 15) of row (t >> 4) of Q and of dO
-  const int srow = tid >> 4, sc = tid & 15;
-  u32x4 xq, xo;
-  float lr = 0.f;
-  // chunk order: query chunks walked backwards from the end of the range,
-  // heads innermost.  Key tiles evicted by the same event share that end, so
-  // workgroups running side by side read the same Q/dO chunks at about the
-  // same time and share them through L2.
-  auto chunk_row = [&](int idx) { return (c_end - 1 - idx / G) * BQ; };
-  auto load_chunk = [&](int idx) {
-    const int h = hkv * G + idx % G;
-    const int c0 = chunk_row(idx);
-    const int row = c0 + srow;
-    const size_t off = (static_cast<size_t>(b) * N + row) * tokq + static_cast<size_t>(h) * D +
-                       sc * 8;
-    const bool ok = row < N;
-    xq = ok ? *reinterpret_cast<const u32x4*>(q + off) : u32x4{0u, 0u, 0u, 0u};
-    xo = ok ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0u, 0u, 0u, 0u};
-    if (tid < 2 * BQ) {
-      const int r2 = c0 + (tid & (BQ - 1));
-      const size_t li = (static_cast<size_t>(b) * Hq + h) * N + r2;
-      if (tid < BQ)
-        lr = r2 < N ? lse[li] * KS_LOG2E : INFINITY;
-      else
-        lr = r2 < N ? di[li] : 0.f;
-    }
-  };
-  auto store_chunk = [&](int buf) {
-    tile_store_chunk(Qs[buf], srow, sc, xq);
-    tile_store_chunk(Os[buf], srow, sc, xo);
-    if (tid < BQ)
-      Ls[buf][tid] = lr;
-    else if (tid < 2 * BQ)
-      Ds[buf][tid - BQ] = lr;
-  };
-
-  auto compute = [&](int buf, int c0) {
+  auto compute = [&](const bf16_t* Qs, int c0) {
     if (c0 >= wq1 || c0 + BQ <= kw0) return;  // none of this wave's keys is seen
+    const bf16_t* Os = Qs + BQ * kTileRow;
     const bool partial = !((c0 >= kmax) && (c0 + BQ <= emn) && (c0 + BQ <= N));
     f32x16 sacc, pacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      sacc = mfma32x32x16(tile_chunk(Qs[buf], la, 0, 2 * s + lh), kf[s], sacc);
-      pacc = mfma32x32x16(tile_chunk(Os[buf], la, 0, 2 * s + lh),
+      sacc = mfma32x32x16(tile_chunk(Qs, la, 0, 2 * s + lh), kf[s], sacc);
+      pacc = mfma32x32x16(tile_chunk(Os, la, 0, 2 * s + lh),
                           tile_chunk(Vst, la, 32 * w, 2 * s + lh), pacc);
     }
-    // lane = key jl; accumulator row r = query c0 + 8 (r / 4) + 4 lh + r % 4
+    // lane = key jl; accumulator row r = query c0 + 8 (r / 4) + 4 lh + r % 4;
+    // LSE / D_i of rows 4m .. 4m + 3 sit in the pad slot of tile position m
     float pv[16];
     if (partial) {  // uniform branch: element mask only on partial chunks
       const int lo = jl - c0, hi = min(ej, N) - c0;  // live iff lo <= row < hi
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][rg * 8 + lh * 4]);
+        const float4 l4 =
+            *reinterpret_cast<const float4*>(Qs + (2 * rg + lh) * kTileRow + 128);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -209,7 +268,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[buf][rg * 8 + lh * 4]);
+        const float4 l4 =
+            *reinterpret_cast<const float4*>(Qs + (2 * rg + lh) * kTileRow + 128);
         pv[rg * 4 + 0] = fast_exp2(fmaf(sacc[rg * 4 + 0], sl2, -l4.x));
         pv[rg * 4 + 1] = fast_exp2(fmaf(sacc[rg * 4 + 1], sl2, -l4.y));
         pv[rg * 4 + 2] = fast_exp2(fmaf(sacc[rg * 4 + 2], sl2, -l4.z));
@@ -219,7 +279,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      const float4 d4 = *reinterpret_cast<const float4*>(&Ds[buf][rg * 8 + lh * 4]);
+      const float4 d4 = *reinterpret_cast<const float4*>(Os + (2 * rg + lh) * kTileRow + 128);
       const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -232,25 +292,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        dva[db] = mfma32x32x16(tile_frag_t(Os[buf], lt, 16 * ks, 32 * db), pf[ks], dva[db]);
-        dka[db] = mfma32x32x16(tile_frag_t(Qs[buf], lt, 16 * ks, 32 * db), sf[ks], dka[db]);
+        dva[db] = mfma32x32x16(tile_frag_t(Os, lt, 16 * ks, 32 * db), pf[ks], dva[db]);
+        dka[db] = mfma32x32x16(tile_frag_t(Qs, lt, 16 * ks, 32 * db), sf[ks], dka[db]);
       }
   };
 
-  if (nchunks > 0) {
-    load_chunk(0);
-    store_chunk(0);
+  __syncthreads();  // V staged
+  // step: own DMA loads of chunk idx have landed (the NBUF - 2 later chunks
+  // may still be in flight); after the barrier every wave's have, and the
+  // buffer read at step idx - 1 is free for chunk idx + NBUF - 1
+#define KS_DKDV_STEP(CUR, NXT)                        \
+  {                                                   \
+    const int idx = base + (CUR##_i);                 \
+    if (idx >= nchunks) break;                        \
+    wait_vm<DMA_PER_WAVE * (NBUF - 2)>();             \
+    bar_nofence();                                    \
+    issue(NXT, idx + NBUF - 1);                       \
+    compute(CUR, chunk_row(idx));                     \
   }
-  __syncthreads();
-  int buf = 0;
-  for (int idx = 0; idx < nchunks; ++idx) {
-    const bool more = idx + 1 < nchunks;
-    if (more) load_chunk(idx + 1);
-    compute(buf, chunk_row(idx));
-    if (more) store_chunk(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+  constexpr int C0_i = 0, C1_i = 1, C2_i = 2, C3_i = 3;
+  for (int base = 0; base < nchunks; base += NBUF) {
+    KS_DKDV_STEP(C0, C3)
+    KS_DKDV_STEP(C1, C0)
+    KS_DKDV_STEP(C2, C1)
+    KS_DKDV_STEP(C3, C2)
   }
+#undef KS_DKDV_STEP
+  wait_vm<0>();  // no DMA write may land after the workgroup ends
 
   // lane holds key jl; rows of dK^T / dV^T are d = 32 db + 8 rg + 4 lh + c
   if (jl < N) {
@@ -278,9 +346,9 @@ template <int HPW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
-    const int32_t* __restrict__ emax, const float* __restrict__ lse,
+    const int32_t* __restrict__ emax, const float* __restrict__ lse2,
     const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
-    int B, int N, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale) {
+    int B, int N, int Npad, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale) {
   constexpr int RS = 8 / HPW;
   constexpr int BM = 32 * RS;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * kTileRow];
@@ -326,8 +394,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       qf[s] = __builtin_bit_cast(bf16x8, a);
       gf[s] = __builtin_bit_cast(bf16x8, c);
     }
-    const size_t li = (static_cast<size_t>(b) * Hq + hq) * N + (qi < N ? qi : 0);
-    l2 = qi < N ? lse[li] * KS_LOG2E : INFINITY;
+    const size_t li = (static_cast<size_t>(b) * Hq + hq) * Npad + (qi < N ? qi : 0);
+    l2 = qi < N ? lse2[li] : INFINITY;
     dii = qi < N ? di[li] : 0.f;
   }
   f32x16 dqa[NDB];
@@ -436,8 +504,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+int padded_rows(int N) { return (N + BQ - 1) / BQ * BQ; }
+
+// D_i and LSE (log2 units), [B][Hq][Npad] floats each
 size_t di_bytes(int B, int N, int Hq) {
-  return (static_cast<size_t>(B) * Hq * N * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return (static_cast<size_t>(B) * Hq * padded_rows(N) * sizeof(float) + 255) &
+         ~static_cast<size_t>(255);
 }
 
 }  // namespace
@@ -450,7 +522,7 @@ extern "C" size_t ks_evict_attn_bwd_workspace(int B, int N, int Hq, int Hkv, int
   (void)Dh;
   (void)dtype;
   if (B <= 0 || N <= 0 || Hq <= 0) return 0;
-  return summary_bytes(B, N) + di_bytes(B, N, Hq);
+  return summary_bytes(B, N) + 2 * di_bytes(B, N, Hq);
 }
 
 extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void* v,
@@ -474,7 +546,7 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   KS_REQUIRE(ks_aligned16(q) && ks_aligned16(k) && ks_aligned16(v) && ks_aligned16(o) &&
                  ks_aligned16(dout) && ks_aligned16(dq) && ks_aligned16(dk) && ks_aligned16(dv),
              "ks_evict_attn_bwd: tensors must be 16-byte aligned");
-  const size_t need = summary_bytes(B, N) + di_bytes(B, N, Hq);
+  const size_t need = summary_bytes(B, N) + 2 * di_bytes(B, N, Hq);
   if (!ws || ws_bytes < need)
     return ks_fail(KS_ERR_WORKSPACE, "ks_evict_attn_bwd: workspace %zu < %zu bytes", ws_bytes,
                    need);
@@ -483,6 +555,8 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   ks_status st = launch_summary(e, ws, B, N, s, &emin, &emax);
   if (st != KS_OK) return st;
   float* di = reinterpret_cast<float*>(static_cast<char*>(ws) + summary_bytes(B, N));
+  float* lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(di) + di_bytes(B, N, Hq));
+  const int Npad = padded_rows(N);
   const int ntiles = (N + kKeyTile - 1) / kKeyTile;
   const bf16_t* qq = static_cast<const bf16_t*>(q);
   const bf16_t* kk = static_cast<const bf16_t*>(k);
@@ -490,9 +564,10 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   const bf16_t* gg = static_cast<const bf16_t*>(dout);
 
   const long long rows = static_cast<long long>(B) * N * Hq;
-  KS_REQUIRE((rows + 15) / 16 < (1LL << 31), "ks_evict_attn_bwd: too many rows");
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0,
-                     s, static_cast<const bf16_t*>(o), gg, di, rows, N, Hq);
+  const long long prows = rows + static_cast<long long>(B) * Hq * (Npad - N);
+  KS_REQUIRE((prows + 15) / 16 < (1LL << 31), "ks_evict_attn_bwd: too many rows");
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3(static_cast<unsigned>((prows + 15) / 16)), dim3(256),
+                     0, s, static_cast<const bf16_t*>(o), gg, lse, di, lse2, rows, N, Npad, Hq);
   st = ks_check_launch("ks_evict_attn_bwd(pre)");
   if (st != KS_OK) return st;
 
@@ -500,8 +575,8 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   const long long nkv = static_cast<long long>(B) * Hkv * nkt;
   KS_REQUIRE(nkv < (1LL << 31), "ks_evict_attn_bwd: grid too large");
   hipLaunchKernelGGL(dkdv_kernel, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq, kk,
-                     vv, e, emin, emax, lse, di, gg, static_cast<bf16_t*>(dk),
-                     static_cast<bf16_t*>(dv), B, N, Hq, Hkv, ntiles, scale);
+                     vv, e, emin, emax, lse2, di, gg, static_cast<bf16_t*>(dk),
+                     static_cast<bf16_t*>(dv), B, N, Npad, Hq, Hkv, ntiles, scale);
   st = ks_check_launch("ks_evict_attn_bwd(dkdv)");
   if (st != KS_OK) return st;
 
@@ -512,8 +587,8 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   KS_REQUIRE(total_q < (1LL << 31), "ks_evict_attn_bwd: grid too large");
 #define KS_DQ_LAUNCH(HPW_)                                                                   \
   hipLaunchKernelGGL((dq_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(512), \
-                     0, s, qq, kk, vv, e, emin, emax, lse, di, gg, static_cast<bf16_t*>(dq), B, \
-                     N, Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
+                     0, s, qq, kk, vv, e, emin, emax, lse2, di, gg, static_cast<bf16_t*>(dq),    \
+                     B, N, Npad, Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
   if (hpw == 4) KS_DQ_LAUNCH(4);
   else if (hpw == 2) KS_DQ_LAUNCH(2);
   else KS_DQ_LAUNCH(1);
