@@ -92,29 +92,6 @@ constexpr int TSLOTS = BQ * (kTileRow / 8);   // 16-byte slots per 32-row tile
 constexpr int CELEMS = 2 * BQ * kTileRow;     // bf16 elements per staged chunk
 constexpr int DMA_PER_WAVE = 3;
 
-__device__ __forceinline__ void lds_dma16(const void* src, bf16_t* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_dst), 16,
-                                   0, 0);
-}
-
-// wait until at most N vector-memory operations of this wave are pending
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
-  // (15 = no wait), vmcnt[5:4] in bits 15:14
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// workgroup barrier without a memory fence: callers order their LDS-DMA
-// loads with wait_vm first; the empty asm statements keep the compiler from
-// moving memory accesses across it
-__device__ __forceinline__ void bar_nofence() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 // packed description of one DMA slot: bit 0..1 kind (0 Q data, 1 dO data,
 // 2 LSE, 3 D_i), bits 2..6 row (data) or 4-row group (LSE, D_i), bits 7..10
 // 16-byte chunk of the row
@@ -179,7 +156,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int dsc2 = dma_slot_desc(1024 + lane);
   // stage chunk min(idx, nchunks - 1) into buffer dst (the tail re-stages the
   // last chunk, so every wave issues the same number of DMA loads per step)
-  auto issue = [&](bf16_t* dst, int idx) {
+  auto issue = [&](lds_bf16_t* dst, int idx) {
     idx = min(idx, nchunks - 1);
     const int h = hkv * G + idx % G;
     const int c0 = chunk_row(idx);
@@ -197,9 +174,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lds_dma16(src(dsc2), dst + 1024 * 8);
   };
   if (nchunks > 0) {
-    issue(C0, 0);
-    issue(C1, 1);
-    issue(C2, 2);
+    issue(lds_ptr(C0), 0);
+    issue(lds_ptr(C1), 1);
+    issue(lds_ptr(C2), 2);
   }
 
   bf16x8 kf[NSTEP];
@@ -301,14 +278,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // step: own DMA loads of chunk idx have landed (the NBUF - 2 later chunks
   // may still be in flight); after the barrier every wave's have, and the
   // buffer read at step idx - 1 is free for chunk idx + NBUF - 1
-#define KS_DKDV_STEP(CUR, NXT)                        \
-  {                                                   \
-    const int idx = base + (CUR##_i);                 \
-    if (idx >= nchunks) break;                        \
-    wait_vm<DMA_PER_WAVE * (NBUF - 2)>();             \
-    bar_nofence();                                    \
-    issue(NXT, idx + NBUF - 1);                       \
-    compute(CUR, chunk_row(idx));                     \
+#define KS_DKDV_STEP(CUR, NXT)                           \
+  {                                                      \
+    const int idx = base + (CUR##_i);                    \
+    wait_vm<DMA_PER_WAVE * (NBUF - 2)>();                \
+    bar_nofence();                                       \
+    issue(lds_ptr(NXT), idx + NBUF - 1);                 \
+    if (idx < nchunks) compute(CUR, chunk_row(idx));     \
   }
   constexpr int C0_i = 0, C1_i = 1, C2_i = 2, C3_i = 3;
   for (int base = 0; base < nchunks; base += NBUF) {
@@ -345,15 +321,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <int HPW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
-    const int32_t* __restrict__ emax, const float* __restrict__ lse2,
-    const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
-    int B, int N, int Npad, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale) {
+    const TileSummary ts, const float* __restrict__ lse2, const float* __restrict__ di,
+    const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq, int B, int N, int Npad, int Hq,
+    int Hkv, int ntiles, int nqt, int total_wg, float scale) {
   constexpr int RS = 8 / HPW;
   constexpr int BM = 32 * RS;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * kTileRow];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * kTileRow];
-  __shared__ __attribute__((aligned(16))) int Es[2][KT];
+  __shared__ __attribute__((aligned(16))) bf16_t S0[kKvElems];
+  __shared__ __attribute__((aligned(16))) bf16_t S1[kKvElems];
+  __shared__ __attribute__((aligned(16))) bf16_t S2[kKvElems];
+  __shared__ __attribute__((aligned(16))) bf16_t S3[kKvElems];
+  __shared__ uint16_t live[kLiveWindow];
+  __shared__ int wsum[8];
 
   int lin = blockIdx.x;
   lin = (lin & 7) * (total_wg >> 3) + (lin >> 3);
@@ -365,7 +343,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int G = Hq / Hkv;
   const int hq0 = grp * HPW;
   const int hkv = hq0 / G;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq = hq0 + (w % HPW);
   const int i0 = qt * BM;
   const int wi0 = i0 + (w / HPW) * 32;
@@ -373,13 +352,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int lq = lane & 31, lh = lane >> 5;
   const int la = tile_lane_a(lane), lt = tile_lane_t(lane);
   const int qi = wi0 + lq;
-  const size_t tokkv = static_cast<size_t>(Hkv) * D;
+  const int tok = Hkv * D;
   const size_t tokq = static_cast<size_t>(Hq) * D;
-  const bf16_t* kb = k + static_cast<size_t>(b) * N * tokkv + static_cast<size_t>(hkv) * D;
-  const bf16_t* vb = v + static_cast<size_t>(b) * N * tokkv + static_cast<size_t>(hkv) * D;
-  const int32_t* eb = e + static_cast<size_t>(b) * N;
-  const int32_t* eminb = emin + static_cast<size_t>(b) * ntiles;
+  const bf16_t* kb = k + static_cast<size_t>(b) * N * tok + static_cast<size_t>(hkv) * D;
+  const bf16_t* vb = v + static_cast<size_t>(b) * N * tok + static_cast<size_t>(hkv) * D;
+  const int32_t* erb = ts.erec + static_cast<size_t>(b) * ntiles * kErec;
+  const int32_t* emaxb = ts.emax + static_cast<size_t>(b) * ntiles;
   const float sl2 = scale * KS_LOG2E;
+  KvStager stg;
+  stg.init(w, lane);
 
   bf16x8 qf[NSTEP], gf[NSTEP];
   float l2, dii;
@@ -398,37 +379,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     l2 = qi < N ? lse2[li] : INFINITY;
     dii = qi < N ? di[li] : 0.f;
   }
+  wait_vm<0>();  // Q, dO in registers before the DMA stream starts
   f32x16 dqa[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqa[db][r] = 0.f;
 
-  u32x4 kr[2], vr[2];
-  int er = 0;
-  auto load_tile = [&](int t) {
+  // kv: staged tile t (K tile, then V tile)
+  auto compute = [&](const bf16_t* kv, int t) {
+    const bf16_t* Vt = kv + KT * kTileRow;
     const int j0 = t * KT;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + 512 * u;
-      const int j = j0 + (idx >> 4), c = idx & 15;
-      const bool ok = j < N;
-      kr[u] = ok ? *reinterpret_cast<const u32x4*>(kb + j * tokkv + c * 8) : u32x4{0u, 0u, 0u, 0u};
-      vr[u] = ok ? *reinterpret_cast<const u32x4*>(vb + j * tokkv + c * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < KT) er = (j0 + tid < N) ? eb[j0 + tid] : 0;
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + 512 * u;
-      tile_store_chunk(Ks[buf], idx >> 4, idx & 15, kr[u]);
-      tile_store_chunk(Vs[buf], idx >> 4, idx & 15, vr[u]);
-    }
-    if (tid < KT) Es[buf][tid] = er;
-  };
-
-  auto body = [&](int buf, int j0, bool partial) {
+    const int emn = __builtin_amdgcn_readfirstlane(staged_emin(kv));
+    const bool partial = !((j0 + KT - 1 <= i0) && (emn >= i1) && (j0 + KT <= N));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       f32x16 sacc, pacc;
@@ -436,8 +399,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
-        sacc = mfma32x32x16(tile_chunk(Ks[buf], la, kk * 32, 2 * s + lh), qf[s], sacc);
-        pacc = mfma32x32x16(tile_chunk(Vs[buf], la, kk * 32, 2 * s + lh), gf[s], pacc);
+        sacc = mfma32x32x16(tile_chunk(kv, la, kk * 32, 2 * s + lh), qf[s], sacc);
+        pacc = mfma32x32x16(tile_chunk(Vt, la, kk * 32, 2 * s + lh), gf[s], pacc);
       }
       // lane = query qi; accumulator row r = key j0 + 32 kk + 8 (r / 4) + 4 lh + r % 4
       float pv[16];
@@ -447,7 +410,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int kl = kk * 32 + rg * 8 + lh * 4;
-          const int4 ev = *reinterpret_cast<const int4*>(&Es[buf][kl]);
+          const int4 ev = staged_e4(kv, kl >> 2);
           const int ee[4] = {ev.x, ev.y, ev.z, ev.w};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
@@ -463,30 +426,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          dqa[db] = mfma32x32x16(tile_frag_t(Ks[buf], lt, kk * 32 + 16 * ks, 32 * db), sf[ks],
+          dqa[db] = mfma32x32x16(tile_frag_t(kv, lt, kk * 32 + 16 * ks, 32 * db), sf[ks],
                                  dqa[db]);
     }
   };
 
-  LiveTiles it;
-  it.init(emax + static_cast<size_t>(b) * ntiles, (i1 - 1) / KT, i0);
-  int t = it.next();
-  if (t >= 0) {
-    load_tile(t);
-    store_tile(0);
+  // live key tiles in windows of kLiveWindow; within a window, tile k is
+  // staged into buffer k % 4 three tile computations before it is used
+  const int tmax = (i1 - 1) / KT;
+  for (int tw = 0; tw <= tmax; tw += kLiveWindow) {
+    const int n = build_live_list(emaxb, tw, min(tmax, tw + kLiveWindow - 1), i0, live, wsum);
+    if (n == 0) continue;
+    auto tile = [&](int kidx) {
+      return __builtin_amdgcn_readfirstlane(tw + live[min(kidx, n - 1)]);
+    };
+    stg.issue(lds_ptr(S0), tile(0), kb, vb, tok, erb, N);
+    stg.issue(lds_ptr(S1), tile(1), kb, vb, tok, erb, N);
+    stg.issue(lds_ptr(S2), tile(2), kb, vb, tok, erb, N);
+    // the window's first loads land before the loop: the compiler then sees
+    // no DMA in flight at the loop head and needs no waits beyond these
+    wait_vm<0>();
+#define KS_DQ_STEP(CUR, NXT, OFF)                             \
+  {                                                           \
+    const int kidx = k0 + (OFF);                              \
+    wait_vm<kKvDma * 2>();                                    \
+    bar_nofence();                                            \
+    stg.issue(lds_ptr(NXT), tile(kidx + 3), kb, vb, tok, erb, N);\
+    if (kidx < n) compute(CUR, tile(kidx));                                 \
   }
-  __syncthreads();
-  int buf = 0;
-  while (t >= 0) {
-    const int tn = it.next();
-    if (tn >= 0) load_tile(tn);
-    const int j0 = t * KT;
-    const int emn = __builtin_amdgcn_readfirstlane(eminb[t]);
-    body(buf, j0, !((j0 + KT - 1 <= i0) && (emn >= i1) && (j0 + KT <= N)));
-    if (tn >= 0) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    t = tn;
+    for (int k0 = 0; k0 < n; k0 += 4) {
+      KS_DQ_STEP(S0, S3, 0)
+      KS_DQ_STEP(S1, S0, 1)
+      KS_DQ_STEP(S2, S1, 2)
+      KS_DQ_STEP(S3, S2, 3)
+    }
+#undef KS_DQ_STEP
+    wait_vm<0>();  // the window's last (re-staged) loads land before reuse
+    bar_nofence();
   }
 
   if (qi < N) {
@@ -550,10 +526,13 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   if (!ws || ws_bytes < need)
     return ks_fail(KS_ERR_WORKSPACE, "ks_evict_attn_bwd: workspace %zu < %zu bytes", ws_bytes,
                    need);
+  KS_REQUIRE(ks_aligned16(ws), "ks_evict_attn_bwd: workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t *emin, *emax;
-  ks_status st = launch_summary(e, ws, B, N, s, &emin, &emax);
+  TileSummary ts;
+  ks_status st = launch_summary(e, ws, B, N, s, &ts);
   if (st != KS_OK) return st;
+  const int32_t* emin = ts.emin;
+  const int32_t* emax = ts.emax;
   float* di = reinterpret_cast<float*>(static_cast<char*>(ws) + summary_bytes(B, N));
   float* lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(di) + di_bytes(B, N, Hq));
   const int Npad = padded_rows(N);
@@ -587,8 +566,8 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   KS_REQUIRE(total_q < (1LL << 31), "ks_evict_attn_bwd: grid too large");
 #define KS_DQ_LAUNCH(HPW_)                                                                   \
   hipLaunchKernelGGL((dq_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(512), \
-                     0, s, qq, kk, vv, e, emin, emax, lse2, di, gg, static_cast<bf16_t*>(dq),    \
-                     B, N, Npad, Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
+                     0, s, qq, kk, vv, ts, lse2, di, gg, static_cast<bf16_t*>(dq), B, N, Npad,   \
+                     Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
   if (hpw == 4) KS_DQ_LAUNCH(4);
   else if (hpw == 2) KS_DQ_LAUNCH(2);
   else KS_DQ_LAUNCH(1);

@@ -35,13 +35,13 @@ namespace ksattn {
 // per-key-tile summary of e
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void tile_summary_kernel(const int32_t* __restrict__ e,
-                                                          int32_t* __restrict__ emin,
-                                                          int32_t* __restrict__ emax, int N,
-                                                          int ntiles) {
+                                                          TileSummary ts, int N, int ntiles) {
   const int t = blockIdx.x, b = blockIdx.y;
   const int j = t * kKeyTile + threadIdx.x;
   const bool ok = j < N;
   const int x = ok ? e[static_cast<size_t>(b) * N + j] : 0;
+  int32_t* rec = ts.erec + (static_cast<size_t>(b) * ntiles + t) * kErec;
+  rec[threadIdx.x] = x;
   int mn = ok ? x : 0x7fffffff;
   int mx = ok ? x : static_cast<int>(0x80000000);
 #pragma unroll
@@ -49,23 +49,29 @@ __global__ __launch_bounds__(64) void tile_summary_kernel(const int32_t* __restr
     mn = min(mn, __shfl_xor(mn, off));
     mx = max(mx, __shfl_xor(mx, off));
   }
+  if (threadIdx.x < 4) rec[kKeyTile + threadIdx.x] = threadIdx.x == 0 ? mn : threadIdx.x == 1 ? mx : 0;
   if (threadIdx.x == 0) {
-    emin[static_cast<size_t>(b) * ntiles + t] = mn;
-    emax[static_cast<size_t>(b) * ntiles + t] = mx;
+    const size_t i = static_cast<size_t>(b) * ntiles + t;
+    ts.emin[i] = mn;
+    ts.emax[i] = mx;
   }
 }
 
 size_t summary_bytes(int B, int N) {
   const size_t nt = (static_cast<size_t>(N) + kKeyTile - 1) / kKeyTile;
-  return ((2 * static_cast<size_t>(B) * nt * sizeof(int32_t)) + 255) & ~static_cast<size_t>(255);
+  const size_t bt = static_cast<size_t>(B) * nt;
+  return (bt * (kErec + 2) * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
 }
 
 ks_status launch_summary(const int32_t* e, void* ws, int B, int N, hipStream_t s,
-                         int32_t** emin, int32_t** emax) {
+                         TileSummary* ts) {
   const int nt = (N + kKeyTile - 1) / kKeyTile;
-  *emin = static_cast<int32_t*>(ws);
-  *emax = *emin + static_cast<size_t>(B) * nt;
-  hipLaunchKernelGGL(tile_summary_kernel, dim3(nt, B), dim3(64), 0, s, e, *emin, *emax, N, nt);
+  const size_t bt = static_cast<size_t>(B) * nt;
+  // 16-byte aligned records first, then the plain minima and maxima
+  ts->erec = static_cast<int32_t*>(ws);
+  ts->emin = ts->erec + bt * kErec;
+  ts->emax = ts->emin + bt;
+  hipLaunchKernelGGL(tile_summary_kernel, dim3(nt, B), dim3(64), 0, s, e, *ts, N, nt);
   return ks_check_launch("eviction-mask tile summary");
 }
 
@@ -427,16 +433,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <int HPW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_d128_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
-    const int32_t* __restrict__ emax, bf16_t* __restrict__ o, float* __restrict__ lse, int B,
-    int N, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float sl2) {
+    const TileSummary ts, bf16_t* __restrict__ o, float* __restrict__ lse, int B, int N, int Hq,
+    int Hkv, int ntiles, int nqt, int total_wg, float sl2) {
   constexpr int D = 128;
   constexpr int RS = 8 / HPW;   // 32-row subtiles per workgroup
   constexpr int BM = 32 * RS;   // query rows per workgroup
   constexpr int KT = kKeyTile;  // 64 keys per tile
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * kTileRow];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * kTileRow];
-  __shared__ __attribute__((aligned(16))) int Es[2][KT];
+  __shared__ __attribute__((aligned(16))) bf16_t S0[kKvElems];
+  __shared__ __attribute__((aligned(16))) bf16_t S1[kKvElems];
+  __shared__ __attribute__((aligned(16))) bf16_t S2[kKvElems];
+  __shared__ __attribute__((aligned(16))) bf16_t S3[kKvElems];
+  __shared__ uint16_t live[kLiveWindow];
+  __shared__ int wsum[8];
 
   int lin = blockIdx.x;
   lin = (lin & 7) * (total_wg >> 3) + (lin >> 3);
@@ -448,7 +456,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int G = Hq / Hkv;
   const int hq0 = grp * HPW;
   const int hkv = hq0 / G;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq = hq0 + (w % HPW);
   const int i0 = qt * BM;
   const int wi0 = i0 + (w / HPW) * 32;
@@ -457,11 +466,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int qi = wi0 + lq;  // this lane's query row
   const int la = tile_lane_a(lane), lt = tile_lane_t(lane);
 
-  const size_t tok = static_cast<size_t>(Hkv) * D;
+  const int tok = Hkv * D;
   const bf16_t* kb = k + static_cast<size_t>(b) * N * tok + static_cast<size_t>(hkv) * D;
   const bf16_t* vb = v + static_cast<size_t>(b) * N * tok + static_cast<size_t>(hkv) * D;
-  const int32_t* eb = e + static_cast<size_t>(b) * N;
-  const int32_t* eminb = emin + static_cast<size_t>(b) * ntiles;
+  const int32_t* erb = ts.erec + static_cast<size_t>(b) * ntiles * kErec;
+  const int32_t* emaxb = ts.emax + static_cast<size_t>(b) * ntiles;
+  KvStager stg;
+  stg.init(w, lane);
 
   // Q as the B operand of S^T = K Q^T: row qi, d = 16 s + 8 lh .. +8
   bf16x8 qf[8];
@@ -475,6 +486,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       qf[s] = __builtin_bit_cast(bf16x8, x);
     }
   }
+  wait_vm<0>();  // Q is in registers before the DMA stream starts
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -482,33 +494,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float mrow = -1e30f, lrow = 0.f;
 
-  // staging: 2 K chunks + 2 V chunks of 16 bytes per thread per tile
-  u32x4 kr[2], vr[2];
-  int er = 0;
-  auto load_tile = [&](int t) {
+  // kv: staged tile t (K tile, then V tile)
+  auto compute = [&](const bf16_t* kv, int t) {
+    const bf16_t* Vt = kv + KT * kTileRow;
     const int j0 = t * KT;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + 512 * u;
-      const int row = idx >> 4, c = idx & 15;
-      const int j = j0 + row;
-      const bool ok = j < N;
-      kr[u] = ok ? *reinterpret_cast<const u32x4*>(kb + j * tok + c * 8) : u32x4{0u, 0u, 0u, 0u};
-      vr[u] = ok ? *reinterpret_cast<const u32x4*>(vb + j * tok + c * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < KT) er = (j0 + tid < N) ? eb[j0 + tid] : 0;
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + 512 * u;
-      tile_store_chunk(Ks[buf], idx >> 4, idx & 15, kr[u]);
-      tile_store_chunk(Vs[buf], idx >> 4, idx & 15, vr[u]);
-    }
-    if (tid < KT) Es[buf][tid] = er;
-  };
-
-  auto compute = [&](int buf, int j0, bool partial) {  // partial: uniform
+    const int emn = __builtin_amdgcn_readfirstlane(staged_emin(kv));
+    const bool partial = !((j0 + KT - 1 <= i0) && (emn >= i1) && (j0 + KT <= N));
     f32x16 sacc[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -516,21 +507,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) sacc[kk][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        sacc[kk] = mfma32x32x16(tile_chunk(Ks[buf], la, kk * 32, 2 * s + lh), qf[s], sacc[kk]);
+        sacc[kk] = mfma32x32x16(tile_chunk(kv, la, kk * 32, 2 * s + lh), qf[s], sacc[kk]);
     }
-    if (partial) {
+    if (partial) {  // uniform branch: element mask only on partial tiles
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int kl = kk * 32 + rg * 8 + lh * 4;
-          const int4 ev = *reinterpret_cast<const int4*>(&Es[buf][kl]);
+          const int4 ev = staged_e4(kv, kl >> 2);
           const int ee[4] = {ev.x, ev.y, ev.z, ev.w};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int j = j0 + kl + c;
-            const bool live = j <= qi && qi < ee[c] && j < N;
-            sacc[kk][rg * 4 + c] = live ? sacc[kk][rg * 4 + c] : -INFINITY;
+            const bool ok = j <= qi && qi < ee[c] && j < N;
+            sacc[kk][rg * 4 + c] = ok ? sacc[kk][rg * 4 + c] : -INFINITY;
           }
         }
     }
@@ -566,28 +557,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        oacc[db] = mfma32x32x16(tile_frag_t(Vs[buf], lt, kk * 16, db * 32), pf[kk], oacc[db]);
+        oacc[db] = mfma32x32x16(tile_frag_t(Vt, lt, kk * 16, db * 32), pf[kk], oacc[db]);
   };
 
-  LiveTiles it;
-  it.init(emax + static_cast<size_t>(b) * ntiles, (i1 - 1) / KT, i0);
-  int t = it.next();
-  if (t >= 0) {
-    load_tile(t);
-    store_tile(0);
+  // live key tiles in windows of kLiveWindow; within a window, tile k is
+  // staged into buffer k % 4 three tile computations before it is used
+  const int tmax = (i1 - 1) / KT;
+  for (int tw = 0; tw <= tmax; tw += kLiveWindow) {
+    const int n = build_live_list(emaxb, tw, min(tmax, tw + kLiveWindow - 1), i0, live, wsum);
+    if (n == 0) continue;
+    auto tile = [&](int kidx) {
+      return __builtin_amdgcn_readfirstlane(tw + live[min(kidx, n - 1)]);
+    };
+    stg.issue(lds_ptr(S0), tile(0), kb, vb, tok, erb, N);
+    stg.issue(lds_ptr(S1), tile(1), kb, vb, tok, erb, N);
+    stg.issue(lds_ptr(S2), tile(2), kb, vb, tok, erb, N);
+    // the window's first loads land before the loop: the compiler then sees
+    // no DMA in flight at the loop head and needs no waits beyond these
+    wait_vm<0>();
+#define KS_FWD_STEP(CUR, NXT, OFF)                          \
+  {                                                         \
+    const int kidx = k0 + (OFF);                            \
+    wait_vm<kKvDma * 2>();                                  \
+    bar_nofence();                                          \
+    stg.issue(lds_ptr(NXT), tile(kidx + 3), kb, vb, tok, erb, N);\
+    if (kidx < n) compute(CUR, tile(kidx));                 \
   }
-  __syncthreads();
-  int buf = 0;
-  while (t >= 0) {
-    const int tn = it.next();
-    if (tn >= 0) load_tile(tn);
-    const int j0 = t * KT;
-    const int emn = __builtin_amdgcn_readfirstlane(eminb[t]);
-    compute(buf, j0, !((j0 + KT - 1 <= i0) && (emn >= i1) && (j0 + KT <= N)));
-    if (tn >= 0) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    t = tn;
+    for (int k0 = 0; k0 < n; k0 += 4) {
+      KS_FWD_STEP(S0, S3, 0)
+      KS_FWD_STEP(S1, S0, 1)
+      KS_FWD_STEP(S2, S1, 2)
+      KS_FWD_STEP(S3, S2, 3)
+    }
+#undef KS_FWD_STEP
+    wait_vm<0>();  // the window's last (re-staged) loads land before reuse
+    bar_nofence();
   }
 
   const float ltot = lrow + __shfl_xor(lrow, 32);
@@ -646,10 +650,13 @@ extern "C" ks_status ks_evict_attn_fwd(const void* q, const void* k, const void*
   if (!ws || ws_bytes < need)
     return ks_fail(KS_ERR_WORKSPACE, "ks_evict_attn_fwd: workspace %zu < %zu bytes", ws_bytes,
                    need);
+  KS_REQUIRE(ks_aligned16(ws), "ks_evict_attn_fwd: workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t *emin, *emax;
-  ks_status st = launch_summary(e, ws, B, N, s, &emin, &emax);
+  TileSummary ts;
+  ks_status st = launch_summary(e, ws, B, N, s, &ts);
   if (st != KS_OK) return st;
+  const int32_t* emin = ts.emin;
+  const int32_t* emax = ts.emax;
   const int ntiles = (N + kKeyTile - 1) / kKeyTile;
   const float sl2 = scale * KS_LOG2E;
   if (dtype == KS_F32) {
@@ -687,7 +694,7 @@ extern "C" ks_status ks_evict_attn_fwd(const void* q, const void* k, const void*
     KS_REQUIRE(total8 < (1LL << 31), "ks_evict_attn_fwd: grid too large");
 #define KS_FWD128_LAUNCH(HPW_)                                                                 \
   hipLaunchKernelGGL((fwd_d128_kernel<HPW_>), dim3(static_cast<unsigned>(total8)), dim3(512), 0, \
-                     s, qq, kk, vv, e, emin, emax, oo, lse, B, N, Hq, Hkv, ntiles, nqt8,          \
+                     s, qq, kk, vv, ts, oo, lse, B, N, Hq, Hkv, ntiles, nqt8,                     \
                      static_cast<int>(total8), sl2)
     if (hpw == 4) KS_FWD128_LAUNCH(4);
     else if (hpw == 2) KS_FWD128_LAUNCH(2);
