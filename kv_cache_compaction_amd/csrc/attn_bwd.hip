@@ -31,13 +31,14 @@ constexpr int KW = 256;        // keys per dK/dV workgroup (8 waves x 32)
 constexpr int KT = kKeyTile;   // keys per dQ tile
 
 // ---------------------------------------------------------------------------
-// D_i = sum_d dO_id O_id (fp32) and LSE in log2 units, both laid out
-// [B][Hq][Npad] with Npad = N rounded up to BQ; padding rows hold 0 so that
-// whole 32-row chunks can be staged without bounds checks.
+// D_i = sum_d dO_id O_id (fp32) and LSE in log2 units, kept as one record
+// per 32-row query chunk of every (batch, head): rec[b][h][c][64] holds the
+// LSE of rows 32 c .. 32 c + 31, then their D_i (256 bytes, one DMA unit).
+// Rows past N (up to Npad = N rounded up to BQ) hold 0.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_pre_kernel(
     const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ di, float* __restrict__ lse2, long long rows, int N, int Npad, int Hq) {
+    float* __restrict__ rec, long long rows, int N, int Npad, int Hq) {
   // 16 threads per (b, i, h) row of D = 128 values; rows past B*N*Hq are padding
   const long long r = static_cast<long long>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
@@ -58,13 +59,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(
     const long long bi = r / Hq;
     const long long b = bi / N, i = bi % N;
     const long long bh = b * Hq + h;
-    di[bh * Npad + i] = acc;
-    lse2[bh * Npad + i] = lse[bh * N + i] * KS_LOG2E;
+    float* r0 = rec + (bh * (Npad / BQ) + i / BQ) * (2 * BQ) + i % BQ;
+    r0[0] = lse[bh * N + i] * KS_LOG2E;
+    r0[BQ] = acc;
   } else if (Npad > N) {
     const long long pr = r - rows;  // padding entry pr of (Npad - N) per (b, h)
     const long long bh = pr / (Npad - N), i = N + pr % (Npad - N);
-    di[bh * Npad + i] = 0.f;
-    lse2[bh * Npad + i] = 0.f;
+    float* r0 = rec + (bh * (Npad / BQ) + i / BQ) * (2 * BQ) + i % BQ;
+    r0[0] = 0.f;
+    r0[BQ] = 0.f;
   }
 }
 
@@ -78,37 +81,33 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(
 // reads.  Workgroups are ordered key-tile major so the heavy prompt tiles
 // (whose queries run to the end of the trace) start first.
 //
-// A staged chunk is a Q tile followed by a dO tile, each 32 rows of 17
-// 16-byte slots (see attn_common.h): 1088 slots, 17 wave-wide DMA
-// instructions.  Wave w fills slots [64 w, 64 w + 64) and [64 (w + 8), ...),
-// and every wave fills the last 64 slots [1024, 1088) with the same bytes:
-// each wave then issues the same 3 unconditional DMA loads per chunk, which
-// keeps the per-wave load count, and the waits built on it, exact.  The pad
-// slot of tile position p < 8 carries LSE (Q tile) or D_i (dO tile) of rows
-// 4p .. 4p + 3; the other pad slots receive a harmless copy of the same.
+// A staged chunk is a Q tile, a dO tile (32 rows each in the padded layout
+// of attn_common.h, 544 16-byte slots each, contiguous) and the chunk's
+// LSE / D_i record.  Every DMA instruction reads from one tensor: Q_j covers
+// slots [64 j, 64 j + 64) (Q only, j = 0..7), M covers [512, 576) (the last
+// 32 Q slots and the first 32 dO slots; each half-wave has its own base),
+// O_j covers [576 + 64 j, 640 + 64 j) (dO only) and R the record.  Pad slots
+// get a copy of a data chunk.  Wave w issues Q_w, O_w and, by w % 2, M or R
+// (four waves write each with the same bytes): 3 DMA loads per wave.
 // ---------------------------------------------------------------------------
 constexpr int NBUF = 4;                       // staged chunks
 constexpr int TSLOTS = BQ * (kTileRow / 8);   // 16-byte slots per 32-row tile
-constexpr int CELEMS = 2 * BQ * kTileRow;     // bf16 elements per staged chunk
+constexpr int RECE = 2 * TSLOTS * 8;          // element offset of the record
+constexpr int CELEMS = RECE + 512;            // bf16 elements per staged chunk
 constexpr int DMA_PER_WAVE = 3;
 
-// packed description of one DMA slot: bit 0..1 kind (0 Q data, 1 dO data,
-// 2 LSE, 3 D_i), bits 2..6 row (data) or 4-row group (LSE, D_i), bits 7..10
-// 16-byte chunk of the row
-__device__ __forceinline__ int dma_slot_desc(int s) {
-  const int tile = s >= TSLOTS ? 1 : 0;
-  const int s2 = s - tile * TSLOTS;
-  const int p = s2 / 17, c = s2 - 17 * p;
-  if (c < 16) return tile | (tile_prow(p) << 2) | (c << 7);
-  return (2 + tile) | ((p & 7) << 2);
+// (row, chunk) of a slot of a 32-row staged tile: bits 0..4 row, 5..8 chunk
+__device__ __forceinline__ int chunk_slot_rc(int s) {
+  const int p = s / 17, c = s - 17 * p;
+  return tile_prow(p) | (min(c, 15) << 5);
 }
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
-    const int32_t* __restrict__ emax, const float* __restrict__ lse2,
-    const float* __restrict__ di, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk,
-    bf16_t* __restrict__ dv, int B, int N, int Npad, int Hq, int Hkv, int ntiles, float scale) {
+    const int32_t* __restrict__ emax, const float* __restrict__ rec,
+    const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int B,
+    int N, int Npad, int Hq, int Hkv, int ntiles, float scale) {
   __shared__ __attribute__((aligned(16))) bf16_t Vst[KW * kTileRow];
   __shared__ __attribute__((aligned(16))) bf16_t C0[CELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t C1[CELEMS];
@@ -149,34 +148,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nchunks = nc * G;
 
   // chunk order: query chunks walked backwards from the end of the range,
-  // heads innermost
-  auto chunk_row = [&](int idx) { return (c_end - 1 - idx / G) * BQ; };
-  const int dsc0 = dma_slot_desc(64 * w + lane);
-  const int dsc1 = dma_slot_desc(64 * (w + 8) + lane);
-  const int dsc2 = dma_slot_desc(1024 + lane);
-  // stage chunk min(idx, nchunks - 1) into buffer dst (the tail re-stages the
-  // last chunk, so every wave issues the same number of DMA loads per step)
-  auto issue = [&](lds_bf16_t* dst, int idx) {
-    idx = min(idx, nchunks - 1);
-    const int h = hkv * G + idx % G;
-    const int c0 = chunk_row(idx);
+  // heads innermost; chunk idx = (query chunk c_end - 1 - idx / G, head
+  // hkv G + idx % G), tracked with counters (no division per step)
+  const int nck = Npad / BQ;
+  const uint32_t rc = static_cast<uint32_t>(chunk_slot_rc(64 * w + lane)) |
+                      (static_cast<uint32_t>(chunk_slot_rc(32 + 64 * w + lane)) << 9) |
+                      (static_cast<uint32_t>(chunk_slot_rc(lane < 32 ? 512 + lane : lane - 32))
+                       << 18);
+  const bool mhi = lane >= 32;  // M: lanes 32..63 take dO slots 0..31
+  const int sel = w & 1;        // 0: M, 1: R
+  auto rcoff = [&](uint32_t d, int lim) {
+    const int r = static_cast<int>(d & 31), c = static_cast<int>((d >> 5) & 15);
+    return static_cast<uint32_t>(min(r, lim) * (tokq * 2) + c * 16);
+  };
+  int ih = 0, ic0 = (c_end - 1) * BQ, ij = 0;  // chunk of the next issue
+  // stage the chunk (head offset hh, first row c0) into buffer dst
+  auto issue = [&](lds_bf16_t* dst, int hh, int c0) {
+    const int h = hkv * G + hh;
     const int lim = N - 1 - c0;  // rows past the end re-read row N - 1
     const size_t rowq = (static_cast<size_t>(b) * N + c0) * tokq + static_cast<size_t>(h) * D;
-    const size_t rowl = (static_cast<size_t>(b) * Hq + h) * Npad + c0;
-    auto src = [&](int d) -> const void* {
-      const int kind = d & 3, r = (d >> 2) & 31, c = d >> 7;
-      if (kind < 2)
-        return (kind ? dout : q) + rowq + (min(r, lim) * tokq + c * 8);
-      return (kind == 3 ? di : lse2) + rowl + 4 * r;
-    };
-    lds_dma16(src(dsc0), dst + 64 * w * 8);
-    lds_dma16(src(dsc1), dst + 64 * (w + 8) * 8);
-    lds_dma16(src(dsc2), dst + 1024 * 8);
+    const char* qc = reinterpret_cast<const char*>(q + rowq);
+    const char* oc = reinterpret_cast<const char*>(dout + rowq);
+    const char* rcb = reinterpret_cast<const char*>(
+        rec + ((static_cast<size_t>(b) * Hq + h) * nck + c0 / BQ) * (2 * BQ));
+    lds_dma16(qc + rcoff(rc, lim), dst + 64 * w * 8);
+    lds_dma16(oc + rcoff(rc >> 9, lim), dst + (TSLOTS + 32 + 64 * w) * 8);
+    const char* mb = mhi ? oc : qc;
+    const uint32_t mo = rcoff(rc >> 18, lim);
+    const uint32_t ro = static_cast<uint32_t>((lane & 15) * 16);
+    lds_dma16((sel ? rcb : mb) + (sel ? ro : mo), dst + (sel ? RECE : 512 * 8));
+  };
+  auto issue_next = [&](lds_bf16_t* dst) {  // the tail re-stages the last chunk
+    issue(dst, ih, ic0);
+    if (ij < nchunks - 1) {
+      ++ij;
+      if (++ih == G) {
+        ih = 0;
+        ic0 -= BQ;
+      }
+    }
   };
   if (nchunks > 0) {
-    issue(lds_ptr(C0), 0);
-    issue(lds_ptr(C1), 1);
-    issue(lds_ptr(C2), 2);
+    issue_next(lds_ptr(C0));
+    issue_next(lds_ptr(C1));
+    issue_next(lds_ptr(C2));
   }
 
   bf16x8 kf[NSTEP];
@@ -215,6 +230,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto compute = [&](const bf16_t* Qs, int c0) {
     if (c0 >= wq1 || c0 + BQ <= kw0) return;  // none of this wave's keys is seen
     const bf16_t* Os = Qs + BQ * kTileRow;
+    const float* Rc = reinterpret_cast<const float*>(Qs + RECE);
     const bool partial = !((c0 >= kmax) && (c0 + BQ <= emn) && (c0 + BQ <= N));
     f32x16 sacc, pacc;
 #pragma unroll
@@ -226,14 +242,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                           tile_chunk(Vst, la, 32 * w, 2 * s + lh), pacc);
     }
     // lane = key jl; accumulator row r = query c0 + 8 (r / 4) + 4 lh + r % 4;
-    // LSE / D_i of rows 4m .. 4m + 3 sit in the pad slot of tile position m
+    // LSE and D_i come from the chunk's record
     float pv[16];
     if (partial) {  // uniform branch: element mask only on partial chunks
       const int lo = jl - c0, hi = min(ej, N) - c0;  // live iff lo <= row < hi
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const float4 l4 =
-            *reinterpret_cast<const float4*>(Qs + (2 * rg + lh) * kTileRow + 128);
+        const float4 l4 = *reinterpret_cast<const float4*>(Rc + rg * 8 + lh * 4);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -245,8 +260,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const float4 l4 =
-            *reinterpret_cast<const float4*>(Qs + (2 * rg + lh) * kTileRow + 128);
+        const float4 l4 = *reinterpret_cast<const float4*>(Rc + rg * 8 + lh * 4);
         pv[rg * 4 + 0] = fast_exp2(fmaf(sacc[rg * 4 + 0], sl2, -l4.x));
         pv[rg * 4 + 1] = fast_exp2(fmaf(sacc[rg * 4 + 1], sl2, -l4.y));
         pv[rg * 4 + 2] = fast_exp2(fmaf(sacc[rg * 4 + 2], sl2, -l4.z));
@@ -256,7 +270,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      const float4 d4 = *reinterpret_cast<const float4*>(Os + (2 * rg + lh) * kTileRow + 128);
+      const float4 d4 = *reinterpret_cast<const float4*>(Rc + BQ + rg * 8 + lh * 4);
       const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -278,13 +292,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // step: own DMA loads of chunk idx have landed (the NBUF - 2 later chunks
   // may still be in flight); after the barrier every wave's have, and the
   // buffer read at step idx - 1 is free for chunk idx + NBUF - 1
+  int ch = 0, cc0 = (c_end - 1) * BQ;  // chunk of the next compute
 #define KS_DKDV_STEP(CUR, NXT)                           \
   {                                                      \
     const int idx = base + (CUR##_i);                    \
     wait_vm<DMA_PER_WAVE * (NBUF - 2)>();                \
     bar_nofence();                                       \
-    issue(lds_ptr(NXT), idx + NBUF - 1);                 \
-    if (idx < nchunks) compute(CUR, chunk_row(idx));     \
+    issue_next(lds_ptr(NXT));                            \
+    if (idx < nchunks) compute(CUR, cc0);                \
+    if (++ch == G) {                                     \
+      ch = 0;                                            \
+      cc0 -= BQ;                                         \
+    }                                                    \
   }
   constexpr int C0_i = 0, C1_i = 1, C2_i = 2, C3_i = 3;
   for (int base = 0; base < nchunks; base += NBUF) {
@@ -321,7 +340,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <int HPW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const TileSummary ts, const float* __restrict__ lse2, const float* __restrict__ di,
+    const TileSummary ts, const float* __restrict__ rec,
     const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq, int B, int N, int Npad, int Hq,
     int Hkv, int ntiles, int nqt, int total_wg, float scale) {
   constexpr int RS = 8 / HPW;
@@ -375,9 +394,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       qf[s] = __builtin_bit_cast(bf16x8, a);
       gf[s] = __builtin_bit_cast(bf16x8, c);
     }
-    const size_t li = (static_cast<size_t>(b) * Hq + hq) * Npad + (qi < N ? qi : 0);
-    l2 = qi < N ? lse2[li] : INFINITY;
-    dii = qi < N ? di[li] : 0.f;
+    const int qr = qi < N ? qi : 0;
+    const float* r0 =
+        rec + ((static_cast<size_t>(b) * Hq + hq) * (Npad / BQ) + qr / BQ) * (2 * BQ) + qr % BQ;
+    l2 = qi < N ? r0[0] : INFINITY;
+    dii = qi < N ? r0[BQ] : 0.f;
   }
   wait_vm<0>();  // Q, dO in registers before the DMA stream starts
   f32x16 dqa[NDB];
@@ -482,7 +503,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 int padded_rows(int N) { return (N + BQ - 1) / BQ * BQ; }
 
-// D_i and LSE (log2 units), [B][Hq][Npad] floats each
+// one of the two halves of the LSE / D_i records, [B][Hq][Npad] floats
 size_t di_bytes(int B, int N, int Hq) {
   return (static_cast<size_t>(B) * Hq * padded_rows(N) * sizeof(float) + 255) &
          ~static_cast<size_t>(255);
@@ -533,8 +554,7 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   if (st != KS_OK) return st;
   const int32_t* emin = ts.emin;
   const int32_t* emax = ts.emax;
-  float* di = reinterpret_cast<float*>(static_cast<char*>(ws) + summary_bytes(B, N));
-  float* lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(di) + di_bytes(B, N, Hq));
+  float* rec = reinterpret_cast<float*>(static_cast<char*>(ws) + summary_bytes(B, N));
   const int Npad = padded_rows(N);
   const int ntiles = (N + kKeyTile - 1) / kKeyTile;
   const bf16_t* qq = static_cast<const bf16_t*>(q);
@@ -546,7 +566,7 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   const long long prows = rows + static_cast<long long>(B) * Hq * (Npad - N);
   KS_REQUIRE((prows + 15) / 16 < (1LL << 31), "ks_evict_attn_bwd: too many rows");
   hipLaunchKernelGGL(bwd_pre_kernel, dim3(static_cast<unsigned>((prows + 15) / 16)), dim3(256),
-                     0, s, static_cast<const bf16_t*>(o), gg, lse, di, lse2, rows, N, Npad, Hq);
+                     0, s, static_cast<const bf16_t*>(o), gg, lse, rec, rows, N, Npad, Hq);
   st = ks_check_launch("ks_evict_attn_bwd(pre)");
   if (st != KS_OK) return st;
 
@@ -554,7 +574,7 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   const long long nkv = static_cast<long long>(B) * Hkv * nkt;
   KS_REQUIRE(nkv < (1LL << 31), "ks_evict_attn_bwd: grid too large");
   hipLaunchKernelGGL(dkdv_kernel, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq, kk,
-                     vv, e, emin, emax, lse2, di, gg, static_cast<bf16_t*>(dk),
+                     vv, e, emin, emax, rec, gg, static_cast<bf16_t*>(dk),
                      static_cast<bf16_t*>(dv), B, N, Npad, Hq, Hkv, ntiles, scale);
   st = ks_check_launch("ks_evict_attn_bwd(dkdv)");
   if (st != KS_OK) return st;
@@ -566,7 +586,7 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   KS_REQUIRE(total_q < (1LL << 31), "ks_evict_attn_bwd: grid too large");
 #define KS_DQ_LAUNCH(HPW_)                                                                   \
   hipLaunchKernelGGL((dq_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(512), \
-                     0, s, qq, kk, vv, ts, lse2, di, gg, static_cast<bf16_t*>(dq), B, N, Npad,   \
+                     0, s, qq, kk, vv, ts, rec, gg, static_cast<bf16_t*>(dq), B, N, Npad,        \
                      Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
   if (hpw == 4) KS_DQ_LAUNCH(4);
   else if (hpw == 2) KS_DQ_LAUNCH(2);
