@@ -139,7 +139,7 @@ def main():
     pos4f = pos4[:, 0].contiguous()
     table0 = torch.from_numpy(db.table0).to(dev)
     nblk0 = torch.from_numpy(db.nblk0).to(dev)
-    keeps = [torch.from_numpy(db.keeps[r]).to(dev) for r in range(db.keeps.shape[0])]
+    keeps_all = torch.from_numpy(np.ascontiguousarray(db.keeps)).to(dev)  # [R, B, MB]
     tbufs = [torch.empty_like(table0), torch.empty_like(table0)]
     nbufs = [torch.empty_like(nblk0), torch.empty_like(nblk0)]
     seq_lens = torch.from_numpy((db.live_len + 1).astype(np.int32)).to(dev)
@@ -154,12 +154,10 @@ def main():
     dec_bytes = int((L * H4kv * D * 2 * 2).sum()) + 2 * DB * H4q * D * 2 + \
         2 * 2 * DB * H4kv * D * 2 + DB * H4q * D * 2 + DB * H4q * 4 + \
         int(((L + 15) // 16).sum()) * 4 + DB * 4
-    comp_bytes = 0
-    nb_cur = db.nblk0.astype(np.int64).copy()
-    for r in range(db.keeps.shape[0]):
-        comp_bytes += int(nb_cur.sum()) * 5 + DB * MB * 4 + DB * 8
-        nb_cur = np.array([int(db.keeps[r, b, :nb_cur[b]].sum()) for b in range(DB)])
-    R = len(keeps)
+    # compaction bytes: the table rows and every event's keep flags read once,
+    # the compacted rows and lengths written once
+    R = db.keeps.shape[0]
+    comp_bytes = DB * MB * 4 + R * DB * MB + DB * MB * 4 + DB * 8
 
     stream = torch.cuda.current_stream()
 
@@ -180,11 +178,10 @@ def main():
         ks.ks_evict_attn_bwd(q, k, v, e, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws_b, stream=stream)
         t1(ev, "attn_bwd")
         ev = t0()
-        src, srcn = table0, nblk0
-        for r in range(R):
-            ks.ks_compact_block_table(src, srcn, keeps[r], tbufs[r % 2], nbufs[r % 2],
-                                      stream=stream)
-            src, srcn = tbufs[r % 2], nbufs[r % 2]
+        # the step's compaction events, applied together in one launch
+        ks.ks_compact_block_table_rounds(table0, nblk0, keeps_all, tbufs[0], nbufs[0],
+                                         stream=stream)
+        src = tbufs[0]
         t1(ev, "compact")
         ev = t0()
         ks.ks_rope_logical(q4, None, pos4, stream=stream)

@@ -167,6 +167,31 @@ ks_status ks_compact_block_table(const int32_t* table_in,
                                  int B, int max_blocks, void* stream);
 
 /*
+ * ks_compact_block_table_rounds -- several compaction events in one launch.
+ *
+ * Same result as `rounds` successive ks_compact_block_table calls, where
+ * event r applies keep[r] to the table left by events 0 .. r-1 (each event
+ * is the splice above; a decoder that has several pending events before its
+ * next step applies them together).  Intermediate tables are never written.
+ *
+ * keep      uint8 [rounds, B, max_blocks]; keep[r][b][x] refers to entry x of
+ *           sequence b's table after r events
+ * rounds    0 .. KS_MAX_ROUNDS; rounds = 0 copies the table (clamped length,
+ *           -1 past it)
+ * max_blocks at most KS_MAX_ROUND_BLOCKS (the row is held on chip)
+ * other arguments and aliasing rules as for ks_compact_block_table.
+ * Errors: KS_ERR_INVALID_ARG for rounds or max_blocks out of range.
+ */
+#define KS_MAX_ROUNDS 64
+#define KS_MAX_ROUND_BLOCKS 4096
+ks_status ks_compact_block_table_rounds(const int32_t* table_in,
+                                        const int32_t* nblk_in,
+                                        const uint8_t* keep, int rounds,
+                                        int32_t* table_out, int32_t* nblk_out,
+                                        const int32_t* pos_in, int32_t* pos_out,
+                                        int B, int max_blocks, void* stream);
+
+/*
  * ks_paged_decode -- one GQA decode step over compacted paged caches.
  *
  * Each sequence attends the first seq_lens[b] tokens reached through its

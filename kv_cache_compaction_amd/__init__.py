@@ -7,7 +7,7 @@ only marshals torch tensors into the C ABI declared in ``include/ks.h``.
 """
 from ._lib import (  # noqa: F401
     KS_BF16, KS_BLOCK, KS_F32, KS_NEVER, KSError, LIB_PATH, header_functions,
-    ks_append_kv, ks_compact_block_table, ks_evict_attn_bwd, ks_evict_attn_bwd_workspace,
-    ks_evict_attn_fwd, ks_evict_attn_fwd_workspace, ks_paged_decode,
-    ks_paged_decode_workspace, ks_rope_logical, load_library,
+    ks_append_kv, ks_compact_block_table, ks_compact_block_table_rounds, ks_evict_attn_bwd,
+    ks_evict_attn_bwd_workspace, ks_evict_attn_fwd, ks_evict_attn_fwd_workspace,
+    ks_paged_decode, ks_paged_decode_workspace, ks_rope_logical, load_library,
 )

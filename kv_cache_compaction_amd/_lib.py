@@ -43,6 +43,7 @@ _SIGS = {
     "ks_evict_attn_bwd_workspace": ([_i, _i, _i, _i, _i, _i], _sz),
     "ks_evict_attn_bwd": ([_vp] * 10 + [_i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
     "ks_compact_block_table": ([_vp] * 7 + [_i, _i, _vp], _i),
+    "ks_compact_block_table_rounds": ([_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp], _i),
     "ks_paged_decode_workspace": ([_i, _i, _i, _i], _sz),
     "ks_paged_decode": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
     "ks_append_kv": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _f, _vp], _i),
@@ -218,6 +219,28 @@ def ks_compact_block_table(table_in, nblk_in, keep, table_out=None, nblk_out=Non
                                     _ptr(nblk_out), _ptr(pos_in), _ptr(pos_out), B, MB,
                                     _stream(stream))
     _check("ks_compact_block_table", st)
+    return table_out, nblk_out, pos_out
+
+
+def ks_compact_block_table_rounds(table_in, nblk_in, keeps, table_out=None, nblk_out=None,
+                                  pos_in=None, pos_out=None, stream=None):
+    """Apply R compaction events at once; keeps is uint8 [R, B, max_blocks], event r
+    indexing the table left by events 0..r-1.  Returns (table_out, nblk_out, pos_out)."""
+    lib = load_library()
+    B, MB = table_in.shape
+    _cuda_contig("table_in", table_in, torch.int32)
+    _cuda_contig("nblk_in", nblk_in, torch.int32)
+    _cuda_contig("keeps", keeps, torch.uint8)
+    _need(keeps.dim() == 3 and tuple(keeps.shape[1:]) == (B, MB) and
+          tuple(nblk_in.shape) == (B,), "keeps/nblk shape")
+    table_out = torch.empty_like(table_in) if table_out is None else table_out
+    nblk_out = torch.empty_like(nblk_in) if nblk_out is None else nblk_out
+    if pos_in is not None and pos_out is None:
+        pos_out = torch.empty_like(pos_in)
+    st = lib.ks_compact_block_table_rounds(_ptr(table_in), _ptr(nblk_in), _ptr(keeps),
+                                           keeps.shape[0], _ptr(table_out), _ptr(nblk_out),
+                                           _ptr(pos_in), _ptr(pos_out), B, MB, _stream(stream))
+    _check("ks_compact_block_table_rounds", st)
     return table_out, nblk_out, pos_out
 
 

@@ -7,8 +7,10 @@
 // reached through the table.
 //
 // Kernel 1 (split): one 64-lane wave per (sequence, group of HPW query heads
-// of one kv head, split of kSplit blocks).  Lane (t, g) = (lane % 16,
-// lane / 16) owns token slot t of every block and the 32 head-dim entries
+// of one kv head, split of kSplit blocks).  The split's block ids are read
+// once, one per lane; each block's id is then taken with readlane.  Lane
+// (t, g) = (lane % 16, lane / 16) owns token slot t of every block and the 32
+// head-dim entries
 // d = 32s + 8g + i (s, i < 4, 8).  Per block each lane issues four 16-byte
 // loads of K and four of V at those entries, so every load instruction covers
 // 64 contiguous bytes of each of the block's 16 token rows.
@@ -25,13 +27,17 @@
 // Kernel 2 (reduce): merges the splits of each (sequence, head).
 //
 // Memory: K and V of every live token are read exactly once per step; the
-// split partials add 4(D+2) bytes per (sequence, head, split).
+// split partials add 4(D+2) bytes per (sequence, head, split).  The grid runs
+// head groups fastest, so the Hkv waves reading the slices of one pool block
+// (Hkv x 16 x D contiguous elements of K, and of V) run side by side, which
+// keeps the DRAM accesses of concurrent waves on the same rows.
 #include "ks_common.h"
 
 namespace {
 
 constexpr int D = 128;
-constexpr int kSplit = 32;     // blocks per split
+constexpr int kSplit = 48;     // blocks per split (the split's block ids fit one wave)
+static_assert(kSplit <= 64, "one block id per lane");
 constexpr float kTau = 8.0f;   // lazy-rescale slack, log2 units
 
 template <int CTRL>
@@ -67,7 +73,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
     float* __restrict__ part_ml, int Hq, int Hkv, int MB, int NB, int nsplit_max,
     float sl2) {
-  const int split = blockIdx.x, hw = blockIdx.y, b = blockIdx.z;
+  const int hw = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int hq0 = hw * HPW;
   const int hkv = hq0 / G;
@@ -95,15 +101,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[h][i] = 0.f;
   }
+  // the split's block ids, one per lane, read once: block blk's id is then a
+  // wave-uniform value, and its K/V loads do not wait on a table load
   const int32_t* trow = table + static_cast<size_t>(b) * MB;
+  const int pids = lane < blk1 - blk0 ? trow[blk0 + lane] : 0;
   bool bad = false;
+  const size_t lane_off = static_cast<size_t>(t) * D + g * 8;
 
   auto load = [&](int blk, BlockRegs& r) {
-    const int pid = trow[blk];
+    const int pid = __builtin_amdgcn_readlane(pids, blk - blk0);
     const bool ok = static_cast<unsigned>(pid) < static_cast<unsigned>(NB);
     bad |= !ok;
-    const size_t off =
-        ((static_cast<size_t>(ok ? pid : 0) * Hkv + hkv) * 16 + t) * D + g * 8;
+    const size_t off = (static_cast<size_t>(ok ? pid : 0) * Hkv + hkv) * 16 * D + lane_off;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       r.k[s] = *reinterpret_cast<const u32x4*>(kpool + off + s * 32);
@@ -312,7 +321,9 @@ extern "C" ks_status ks_paged_decode(const void* q, const void* k_pool, const vo
       (reinterpret_cast<uintptr_t>(part_ml + 2 * slots) + 255) & ~static_cast<uintptr_t>(255));
   const float sl2 = scale * KS_LOG2E;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(nsplit, Hq / hpw, B);
+  // head groups fastest: the waves that read the kv-head slices of the same
+  // pool blocks (contiguous in memory) are dispatched together
+  const dim3 grid(Hq / hpw, nsplit, B);
   const bf16_t* qq = static_cast<const bf16_t*>(q);
   const bf16_t* kp = static_cast<const bf16_t*>(k_pool);
   const bf16_t* vp = static_cast<const bf16_t*>(v_pool);

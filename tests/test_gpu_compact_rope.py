@@ -59,6 +59,63 @@ def test_compact_cfg4_rounds_pingpong():
     assert np.array_equal(16 * (rn.astype(np.int64) - 1), db.live_len.astype(np.int64))
 
 
+def _oracle_rounds(table, nblk, keeps, pos=None):
+    """Events applied one by one with the oracle's single-event splice; with no
+    event the table is only normalised (-1 past its length), i.e. an all-keep
+    splice."""
+    if keeps.shape[0] == 0:
+        keeps = np.ones((1,) + table.shape, np.uint8)
+    t, n, p = table, nblk, pos
+    for r in range(keeps.shape[0]):
+        t2, n2 = O.compact_block_table(t, n, keeps[r])
+        if p is not None:
+            p, _ = O.compact_block_table(p, n, keeps[r])
+        t, n = t2, n2
+    return t, n, p
+
+
+def test_compact_rounds_cfg4_one_launch():
+    """All events of the decode workload in one launch equal the event-by-event oracle."""
+    db = build_decode_batch(np.random.default_rng(1004), 64)
+    B, MB = db.table0.shape
+    pos0 = np.tile(np.arange(MB, dtype=np.int32), (B, 1))
+    out, n, pos = ks.ks_compact_block_table_rounds(_gpu(db.table0), _gpu(db.nblk0),
+                                                   _gpu(db.keeps), pos_in=_gpu(pos0))
+    rt, rn, rp = _oracle_rounds(db.table0, db.nblk0, db.keeps, pos0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), rt)
+    np.testing.assert_array_equal(n.cpu().numpy(), rn)
+    np.testing.assert_array_equal(pos.cpu().numpy(), rp)
+
+
+@pytest.mark.parametrize("B,MB,R,seed", [(1, 1, 1, 0), (3, 5, 0, 1), (4, 4096, 3, 2),
+                                         (5, 1001, 12, 3), (2, 64, 64, 4), (6, 333, 8, 5)])
+def test_compact_rounds_random_and_edges(B, MB, R, seed):
+    """R events in one launch vs the oracle: ragged widths, zero events, more
+    events than are preloaded, the widest row, empty and clamped lengths."""
+    rng = np.random.default_rng(100 + seed)
+    table = rng.integers(0, 2**31 - 1, size=(B, MB)).astype(np.int32)
+    pos = rng.integers(0, 2**31 - 1, size=(B, MB)).astype(np.int32)
+    nblk = rng.integers(0, MB + 1, size=B).astype(np.int32)
+    nblk[0] = MB
+    if B > 1:
+        nblk[1] = 0
+    if B > 4:
+        nblk[4] = MB + 7     # clamped to MB
+    keeps = (rng.random((R, B, MB)) < 0.85).astype(np.uint8)
+    if B > 2 and R > 0:
+        keeps[:, 2] = 1
+    if B > 3 and R > 1:
+        keeps[1, 3] = 0
+    out, n, po = ks.ks_compact_block_table_rounds(_gpu(table), _gpu(nblk), _gpu(keeps),
+                                                  pos_in=_gpu(pos))
+    rt, rn, rp = _oracle_rounds(table, np.clip(nblk, 0, MB), keeps, pos)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), rt)
+    np.testing.assert_array_equal(n.cpu().numpy(), rn)
+    np.testing.assert_array_equal(po.cpu().numpy(), rp)
+
+
 @pytest.mark.parametrize("B,MB,seed", [(1, 1, 0), (3, 5, 1), (7, 4096, 2), (2, 10000, 3),
                                        (5, 4097, 4)])
 def test_compact_random_and_edges(B, MB, seed):

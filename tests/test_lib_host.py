@@ -103,3 +103,18 @@ def test_append_argument_checks(lib):
     assert st == 1  # base must exceed 1
     st, _ = _status(lib, "ks_append_kv", *([FAKE] * 7), 0, 8, 128, 10, 100, 1, 10000.0, None)
     assert st == 0  # nothing to do
+
+
+def test_compaction_rounds_argument_checks(lib):
+    st, msg = _status(lib, "ks_compact_block_table_rounds", FAKE, FAKE, FAKE, 65, FAKE,
+                      ctypes.c_void_p(1 << 20), None, None, 4, 32, None)
+    assert st == 1 and "rounds" in msg
+    st, msg = _status(lib, "ks_compact_block_table_rounds", FAKE, FAKE, FAKE, 2, FAKE,
+                      ctypes.c_void_p(1 << 20), None, None, 4, 4097, None)
+    assert st == 1 and "max_blocks" in msg
+    st, msg = _status(lib, "ks_compact_block_table_rounds", FAKE, FAKE, FAKE, 2, FAKE, FAKE,
+                      None, None, 4, 32, None)
+    assert st == 1 and "alias" in msg
+    st, _ = _status(lib, "ks_compact_block_table_rounds", None, None, None, 3, None, None, None,
+                    None, 0, 32, None)
+    assert st == 0  # B == 0 is a no-op
