@@ -59,6 +59,73 @@ def live_pairs(e: np.ndarray) -> int:
     return tot
 
 
+def executed_flops(e: np.ndarray, Hq: int, Hkv: int, D: int, kt: int = 64):
+    """MFMA flops the attention kernels execute (tile granularity) for a batch
+    of traces, following their tiling: the forward and dQ kernels visit, per
+    query tile of BM rows and query head, every key tile t with t <= last row
+    / kt and max e over the tile > first row; dK/dV workgroups of 256 keys
+    (8 waves x 32 keys) visit 32-row query chunks of each of the G heads up to
+    the largest e of their keys, each wave skipping chunks none of its keys
+    sees.  Returns (forward, dQ, dK/dV) flops."""
+    G = Hq // Hkv
+    hpw = 4 if G >= 4 else G
+    bm = 32 * (8 // hpw)
+    fwd = dq = dkdv = 0
+    for row in e.astype(np.int64):
+        N = row.size
+        nt = (N + kt - 1) // kt
+        emax = np.array([row[t * kt:(t + 1) * kt].max() for t in range(nt)])
+        for i0 in range(0, N, bm):
+            i1 = min(N, i0 + bm)
+            tmax = (i1 - 1) // kt
+            live = int((emax[:tmax + 1] > i0).sum())
+            fwd += live * 4 * D * bm * kt * Hq
+            dq += live * 6 * D * bm * kt * Hq
+        for j0 in range(0, N, 256):
+            c_begin = j0 // 32
+            c_end = (min(N, int(row[j0:j0 + 256].max())) + 31) // 32
+            for w in range(8):
+                kw0 = j0 + 32 * w
+                keys = row[kw0:min(N, kw0 + 32)]
+                if keys.size == 0:
+                    continue
+                wq1 = min(N, int(keys.max()))
+                c = np.arange(c_begin, c_end) * 32
+                visited = int(((c < wq1) & (c + 32 > kw0)).sum())
+                dkdv += visited * G * 8 * D * 32 * 32 * Hkv
+    return fwd, dq, dkdv
+
+
+def kernel_sources_hash() -> str:
+    """sha256 over the HIP sources of libks (a stored counter summary applies
+    only to the kernels it was taken on)."""
+    import hashlib
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kv_cache_compaction_amd",
+                        "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(root)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(root, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or it was taken on other kernel sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "hbm_traffic_cfg3_cfg4.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_hash():
+        return None
+    ent = rec.get("entry_points", {}).get(kernel)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
 class Timer:
     """HIP-event timing of one stage on the current stream."""
 
@@ -119,6 +186,7 @@ def main():
     ws_b = torch.empty(ks.ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
                        dtype=torch.uint8, device=dev)
     pairs = live_pairs(e_np)
+    ex_fwd, ex_dq, ex_dkdv = executed_flops(e_np, Hq, Hkv, D)
     # live pairs summed over the traces; every query head sees its trace's mask
     flops_fwd = 4.0 * D * pairs * Hq
     flops_bwd = 10.0 * D * pairs * Hq
@@ -213,6 +281,27 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     tot = tm.totals()
+
+    # standalone compaction scan of 2^26 table entries (16384 rows x 4096),
+    # one event, 70% of blocks kept: a bandwidth-meaningful size for the
+    # prefix-scan kernel (not part of the step)
+    crng = np.random.default_rng(4242)
+    CB, CM = 16384, 4096
+    ctab = torch.from_numpy(crng.integers(0, 2**31 - 1, size=(CB, CM), dtype=np.int32)).to(dev)
+    ckeep = torch.from_numpy((crng.random((CB, CM)) < 0.7).astype(np.uint8)).to(dev)
+    cn = torch.full((CB,), CM, dtype=torch.int32, device=dev)
+    cout, cnout = torch.empty_like(ctab), torch.empty_like(cn)
+    ks.ks_compact_block_table(ctab, cn, ckeep, cout, cnout, stream=stream)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        ks.ks_compact_block_table(ctab, cn, ckeep, cout, cnout, stream=stream)
+    c1.record()
+    torch.cuda.synchronize()
+    scan_ms = c0.elapsed_time(c1) / 10
+    scan_bytes = CB * CM * (4 + 1 + 4) + CB * 8
+    del ctab, ckeep, cout
     K = args.steps
     ms = {kk: vv / K for kk, vv in tot.items()}
     attn_ms = ms["attn_fwd"] + ms["attn_bwd"]
@@ -229,6 +318,8 @@ def main():
                    "achieved": dec_bytes / (ms["decode"] * 1e-3) / 1e9, "unit": "GB/s"},
         "compact": {"bound": "hbm", "ms": ms["compact"],
                     "achieved": comp_bytes / (ms["compact"] * 1e-3) / 1e9, "unit": "GB/s"},
+        "compact_2^26": {"bound": "hbm", "ms": scan_ms,
+                         "achieved": scan_bytes / (scan_ms * 1e-3) / 1e9, "unit": "GB/s"},
         "rope": {"bound": "hbm", "ms": ms["rope"],
                  "achieved": 2 * (q.numel() + k.numel()) * 2 / (ms["rope"] * 1e-3) / 1e9,
                  "unit": "GB/s"},
@@ -236,6 +327,13 @@ def main():
     for p in parts.values():
         peak = MFMA_BF16_PEAK_TFLOPS if p["bound"] == "mfma" else HBM_PEAK_GBS
         p["frac"] = p["achieved"] / peak
+    # executed MFMA work (tile granularity) next to the useful work
+    parts["attn_fwd"]["executed_tflop"] = ex_fwd / 1e12
+    parts["attn_fwd"]["executed_over_useful"] = ex_fwd / flops_fwd
+    parts["attn_fwd"]["executed_tflops_per_s"] = ex_fwd / (ms["attn_fwd"] * 1e-3) / 1e12
+    parts["attn_bwd"]["executed_tflop"] = (ex_dq + ex_dkdv) / 1e12
+    parts["attn_bwd"]["executed_over_useful"] = (ex_dq + ex_dkdv) / flops_bwd
+    parts["attn_bwd"]["executed_tflops_per_s"] = (ex_dq + ex_dkdv) / (ms["attn_bwd"] * 1e-3) / 1e12
     dom = max(("attn_fwd", "attn_bwd"), key=lambda x: ms[x])
     result = {
         "metric": "eviction-masked attn fwd+bwd TFLOP/s @32k trace; paged-decode HBM GB/s",
@@ -267,7 +365,8 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(parts[dom]["frac"], 4),
-            "traffic": None,
+            "traffic": stored_traffic(
+                f"ks_{'evict_attn_bwd' if dom == 'attn_bwd' else 'evict_attn_fwd'}"),
         },
         "stages": {kk: {x: (round(y, 4) if isinstance(y, float) else y) for x, y in vv.items()}
                    for kk, vv in parts.items()},
@@ -318,11 +417,21 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
         heads_used += 1
     el = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(14.0 * D * done_pairs / el / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
+        "host": f"{model}; {len(os.sched_getaffinity(0))} logical CPUs available",
         "sample": f"fp64 oracle forward + backward (dQ, dK, dV) of the first {n} tokens "
                   f"of trace 0, {heads_used} query head(s) of kv group 0: {done_pairs} live "
                   f"pairs in {el:.1f} s",
