@@ -12,8 +12,10 @@ Prints one JSON line.  `value` is the masked attention fwd+bwd throughput in
 TFLOP/s of useful work (4*D flops forward and 10*D backward per live
 (query, key) pair per query head; masked pairs are not counted), timed with
 HIP events on the stream the kernels run on.  The decode side's HBM GB/s is
-reported beside it.  `cpu_baseline` times the fp64 oracle on a bounded
-sample of the same workload on the host cores.
+reported beside it.  `reprefill_counterfactual` times, outside the step, the
+attention that re-prefill compaction would run on the same rollouts.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload
+on the host cores.
 """
 from __future__ import annotations
 
@@ -371,9 +373,71 @@ def main():
         "stages": {kk: {x: (round(y, 4) if isinstance(y, float) else y) for x, y in vv.items()}
                    for kk, vv in parts.items()},
     }
+    result["reprefill_counterfactual"] = reprefill_counterfactual(
+        ks, torch, traces, q, k, v, do, stream, ms, pairs, c3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(traces, seeds, c3, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def reprefill_counterfactual(ks, torch, traces, q, k, v, do, stream, ms, pairs, cfg,
+                             reps=3):
+    """Time what re-prefill compaction would run on the same rollouts (paper
+    page, Fig. 2A and Fig. 3): after every event the kept tokens are processed
+    again, as the start of a new causal trace.  The segments are packed end to
+    end (each key evicted at its segment's end), so one masked fwd+bwd launch
+    computes every segment's causal attention; compared with the single
+    masked pass over the rollout that the step times."""
+    from workloads import reprefill_pack, reprefill_segments
+
+    B, N, Hq, Hkv, D = cfg.batch, cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+    packs = [reprefill_pack(tr) for tr in traces]
+    L = max(len(p[0]) for p in packs)
+    packs = [reprefill_pack(tr, L) for tr in traces]
+    dev = q.device
+    idx = torch.from_numpy(np.stack([p[0] for p in packs])).to(dev)
+    ep = torch.from_numpy(np.stack([p[1] for p in packs])).to(dev)
+    gather = lambda t: torch.stack([t[b, idx[b]] for b in range(B)]).contiguous()
+    qp, kp, vp, dop = gather(q), gather(k), gather(v), gather(do)
+    op = torch.empty_like(qp)
+    lsep = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    dqp, dkp, dvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+    wsf = torch.empty(ks.ks_evict_attn_fwd_workspace(B, L, Hq, Hkv, D, ks.KS_BF16),
+                      dtype=torch.uint8, device=dev)
+    wsb = torch.empty(ks.ks_evict_attn_bwd_workspace(B, L, Hq, Hkv, D, ks.KS_BF16),
+                      dtype=torch.uint8, device=dev)
+
+    def run():
+        ks.ks_evict_attn_fwd(qp, kp, vp, ep, out=op, lse=lsep, ws=wsf, stream=stream)
+        ks.ks_evict_attn_bwd(qp, kp, vp, ep, op, lsep, dop, dq=dqp, dk=dkp, dv=dvp, ws=wsb,
+                             stream=stream)
+    run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_rp = ev0.elapsed_time(ev1) / reps
+    segs = [reprefill_segments(tr) for tr in traces]
+    pairs_rp = sum(len(x) * (len(x) + 1) // 2 for sg in segs for x in sg)
+    toks = sum(len(x) for sg in segs for x in sg)
+    t_ks = ms["attn_fwd"] + ms["attn_bwd"]
+    ev = [len(tr.events) for tr in traces]
+    return {
+        "what": "masked fwd+bwd over every re-prefill segment (kept tokens processed "
+                "again after each event) vs one masked pass over the rollout",
+        "packed_len": int(L),
+        "events_per_trace": ev,
+        "fig3_factor": round(N / (cfg.budget - (cfg.overlap + cfg.summary)), 3),
+        "tokens_ratio": round(toks / (B * N), 4),
+        "live_pairs_ratio": round(pairs_rp / pairs, 4),
+        "ms_fwd_bwd": round(t_rp, 3),
+        "ms_fwd_bwd_kv_streams": round(t_ks, 3),
+        "time_ratio": round(t_rp / t_ks, 4),
+        "tflops_useful": round(14.0 * D * pairs_rp * Hq / (t_rp * 1e-3) / 1e12, 2),
+    }
 
 
 def cpu_baseline(traces, seeds, cfg, budget_s):

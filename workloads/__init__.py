@@ -2,12 +2,13 @@
 
 This package builds inputs only: turn boundaries, compaction-event records
 (the per-token eviction index e_j), paged block tables with per-round keep
-flags, and random tensors.  It holds none of the method's arithmetic (no RoPE,
+flags, the segment traces of the re-prefill counterfactual, and random tensors.  It holds none of the method's arithmetic (no RoPE,
 no attention, no table compaction); the oracle and the HIP library each
 implement those on their own.
 """
 from .traces import (  # noqa: F401
     KS_NEVER, BLOCK, Trace, build_trace, check_trace, DecodeBatch, evict_units,
-    build_decode_batch, normal_tensor, trace_blocks_keep,
+    build_decode_batch, normal_tensor, reprefill_pack, reprefill_segments,
+    trace_blocks_keep,
 )
 from .configs import CONFIGS, Config, config_trace_batch, stacked_e  # noqa: F401

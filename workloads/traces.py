@@ -177,6 +177,54 @@ def trace_blocks_keep(tr: Trace) -> np.ndarray:
     return (pad.reshape(nb, BLOCK) == KS_NEVER).all(axis=1).astype(np.uint8)
 
 
+def reprefill_segments(tr: Trace) -> list:
+    """The separate training traces of re-prefill compaction on the same
+    rollout (paper page, Fig. 2A: retained tokens are recomputed and every
+    compaction starts a new trace).  Segment 0 is tokens [0, t_1); segment k
+    is the tokens kept at event t_k -- {j < t_k : e_j > t_k}, re-prefilled in
+    order -- followed by the new tokens [t_k, t_(k+1)) (t_(K+1) = N).  Returns
+    a list of int64 arrays of trace token indices, one per segment; each is a
+    plain causal sequence of its own."""
+    ev = list(tr.events)
+    bounds = [0] + ev + [tr.N]
+    segs = []
+    e = tr.e.astype(np.int64)
+    for k in range(len(bounds) - 1):
+        t, t_next = bounds[k], bounds[k + 1]
+        kept = np.nonzero(e[:t] > t)[0] if k > 0 else np.zeros(0, np.int64)
+        segs.append(np.concatenate([kept, np.arange(t, t_next)]).astype(np.int64))
+    return segs
+
+
+def reprefill_pack(tr: Trace, length: int | None = None):
+    """The re-prefill segments of ``tr`` laid end to end in one sequence.
+
+    Key ``j`` of the packed sequence gets the end of its segment as its
+    eviction index, so under the rule j <= i < e_j every query sees exactly
+    the earlier keys of its own segment: one masked pass over the packed
+    sequence is the separate causal passes of the segments.  ``length`` pads
+    the sequence on the right; a pad token is seen by itself only
+    (e_j = j + 1), so it adds no work beyond its own diagonal tile and no
+    row is empty.
+
+    Returns ``(index, e)``: ``index[p]`` is the rollout token at packed
+    position ``p`` (0 for pads), ``e`` the int32 eviction indices.
+    """
+    segs = reprefill_segments(tr)
+    n = sum(len(x) for x in segs)
+    length = n if length is None else int(length)
+    if length < n:
+        raise ValueError(f"length {length} < packed size {n}")
+    index = np.zeros(length, np.int64)
+    e = np.arange(1, length + 1, dtype=np.int64)
+    p = 0
+    for x in segs:
+        index[p:p + len(x)] = x
+        e[p:p + len(x)] = p + len(x)
+        p += len(x)
+    return index, e.astype(np.int32)
+
+
 @dataclass
 class DecodeBatch:
     """Paged caches of several sequences before a run of compaction rounds.
