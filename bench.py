@@ -12,7 +12,9 @@ Prints one JSON line.  `value` is the masked attention fwd+bwd throughput in
 TFLOP/s of useful work (4*D flops forward and 10*D backward per live
 (query, key) pair per query head; masked pairs are not counted), timed with
 HIP events on the stream the kernels run on.  The decode side's HBM GB/s is
-reported beside it.  `reprefill_counterfactual` times, outside the step, the
+reported beside it.  `single_token_blocks` times the same decode step with
+one pool slot per token (token tables, token-run compaction), and
+`reprefill_counterfactual` times, outside the step, the
 attention that re-prefill compaction would run on the same rollouts.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same workload
 on the host cores.
@@ -373,11 +375,90 @@ def main():
         "stages": {kk: {x: (round(y, 4) if isinstance(y, float) else y) for x, y in vv.items()}
                    for kk, vv in parts.items()},
     }
+    result["single_token_blocks"] = token_granular_decode(ks, torch, stream, c4)
     result["reprefill_counterfactual"] = reprefill_counterfactual(
         ks, torch, traces, q, k, v, do, stream, ms, pairs, c3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(traces, seeds, c3, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def token_granular_decode(ks, torch, stream, cfg, reps=5):
+    """The decode step of the 64-sequence batch with single-token blocks (the
+    SGLang setup: token tables, no padding): every event compacts the token
+    tables (all events in one launch, rows of up to 65k entries), then RoPE of q,
+    append of the new token and the decode.  Timed apart from the step; HBM
+    bytes as for the 16-token decode, with one table entry per token."""
+    from workloads import build_decode_batch, normal_tensor
+
+    db = build_decode_batch(np.random.default_rng(1000 + 4), cfg.batch, block=1)
+    B, MT = db.table0.shape
+    NT = db.num_pool_blocks
+    Hq, Hkv, D = cfg.Hq, cfg.Hkv, cfg.D
+    bf = torch.bfloat16
+    dev = "cuda"
+    kp = normal_tensor((NT, Hkv, D), 8001, 0.5, bf, dev)
+    vp = normal_tensor((NT, Hkv, D), 8002, 0.5, bf, dev)
+    q = normal_tensor((B, 1, Hq, D), 8003, 0.5, bf, dev)
+    k_new = normal_tensor((B, Hkv, D), 8004, 0.5, bf, dev)
+    v_new = normal_tensor((B, Hkv, D), 8005, 0.5, bf, dev)
+    pos = torch.from_numpy(db.pos.astype(np.int32)).to(dev)
+    pos2 = pos[:, None].contiguous()
+    table0 = torch.from_numpy(db.table0).to(dev)
+    n0 = torch.from_numpy(db.nblk0).to(dev)
+    keeps = torch.from_numpy(np.ascontiguousarray(db.keeps)).to(dev)     # [R, B, MT]
+    R = keeps.shape[0]
+    tb, nb = torch.empty_like(table0), torch.empty_like(n0)
+    seq_lens = torch.from_numpy((db.live_len + 1).astype(np.int32)).to(dev)
+    out = torch.empty((B, Hq, D), dtype=bf, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(ks.ks_paged_decode_bs1_workspace(B, Hq, D, MT), dtype=torch.uint8,
+                     device=dev)
+    q0 = q[:, 0]
+
+    def compact():
+        # the pending events applied together in one launch
+        ks.ks_compact_block_table_rounds(table0, n0, keeps, tb, nb, stream=stream)
+        return tb
+
+    def decode(tab):
+        ks.ks_rope_logical(q, None, pos2, stream=stream)
+        ks.ks_append_kv_bs1(k_new, v_new, pos, tab, seq_lens, kp, vp, stream=stream)
+        ks.ks_paged_decode_bs1(q0, kp, vp, tab, seq_lens, out=out, lse=lse, ws=ws,
+                               stream=stream)
+    tab = compact()
+    decode(tab)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_c = t_d = 0.0
+    for _ in range(reps):
+        ev[0].record(stream)
+        tab = compact()
+        ev[1].record(stream)
+        decode(tab)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_c += ev[0].elapsed_time(ev[1])
+        t_d += ev[1].elapsed_time(ev[2])
+    t_c, t_d = t_c / reps, t_d / reps
+    L = db.live_len.astype(np.int64) + 1
+    dec_bytes = int((L * Hkv * D * 2 * 2).sum()) + 2 * B * Hq * D * 2 + \
+        2 * 2 * B * Hkv * D * 2 + B * Hq * D * 2 + B * Hq * 4 + int(L.sum()) * 4 + B * 4
+    # the table rows and every event's keep flags read once, the rows and
+    # lengths written once
+    comp_bytes = B * MT * 4 + R * B * MT + B * MT * 4 + B * 8
+    return {
+        "workload": "64 token-table caches (4k-16k live tokens at any length, 1-6 events "
+                    "of token runs, applied in one launch), 32 q / 8 kv heads, D=128",
+        "events": R,
+        "table_entries": int(MT),
+        "compact_ms": round(t_c, 4),
+        "decode_ms": round(t_d, 4),
+        "compact_gbs": round(comp_bytes / (t_c * 1e-3) / 1e9, 1),
+        "decode_gbs": round(dec_bytes / (t_d * 1e-3) / 1e9, 1),
+        "decode_plus_compact_frac": round((dec_bytes + comp_bytes) / ((t_c + t_d) * 1e-3)
+                                          / 1e9 / HBM_PEAK_GBS, 4),
+    }
 
 
 def reprefill_counterfactual(ks, torch, traces, q, k, v, do, stream, ms, pairs, cfg,

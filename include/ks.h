@@ -159,6 +159,11 @@ ks_status ks_evict_attn_bwd(const void* q, const void* k, const void* v,
  *                      nblk_in are clamped to [0, max_blocks]
  * keep                 uint8 [B, max_blocks], nonzero = keep
  * pos_in, pos_out      int32 [B, max_blocks] or both NULL
+ *
+ * With single-token blocks (the SGLang setup: explainer, paragraph on padding
+ * completions to whole blocks) the same call compacts token tables: entries
+ * are pool slots, one per token, and max_blocks is the row length in tokens.
+ * Rows longer than 4096 entries are split over several workgroups.
  */
 ks_status ks_compact_block_table(const int32_t* table_in,
                                  const int32_t* nblk_in, const uint8_t* keep,
@@ -178,12 +183,15 @@ ks_status ks_compact_block_table(const int32_t* table_in,
  *           sequence b's table after r events
  * rounds    0 .. KS_MAX_ROUNDS; rounds = 0 copies the table (clamped length,
  *           -1 past it)
- * max_blocks at most KS_MAX_ROUND_BLOCKS (the row is held on chip)
+ * max_blocks at most KS_MAX_ROUND_BLOCKS: rows of up to 4096 entries are held
+ *           on chip; longer rows (token tables of single-token blocks) keep
+ *           one survival bit per entry on chip and read the row once at the
+ *           end
  * other arguments and aliasing rules as for ks_compact_block_table.
  * Errors: KS_ERR_INVALID_ARG for rounds or max_blocks out of range.
  */
 #define KS_MAX_ROUNDS 64
-#define KS_MAX_ROUND_BLOCKS 4096
+#define KS_MAX_ROUND_BLOCKS 65536
 ks_status ks_compact_block_table_rounds(const int32_t* table_in,
                                         const int32_t* nblk_in,
                                         const uint8_t* keep, int rounds,
@@ -241,6 +249,46 @@ ks_status ks_append_kv(const void* k_new, const void* v_new, const int32_t* pos,
                        const int32_t* table, const int32_t* seq_lens, void* k_pool,
                        void* v_pool, int B, int Hkv, int D, int max_blocks,
                        int num_pool_blocks, int dtype, float base, void* stream);
+
+/*
+ * ks_paged_decode_bs1 -- ks_paged_decode with single-token blocks.
+ *
+ * The SGLang setup stores one token per block, so turns need no padding to
+ * 16 and compaction can splice any token run (explainer, paragraph on
+ * padding completions to whole blocks).  The table lists one pool slot per
+ * token; everything else is as for ks_paged_decode.
+ *
+ * q           [B, Hq, D] bf16 (rotated)
+ * k_pool,
+ * v_pool      [num_pool_tokens, Hkv, D] bf16 (keys rotated when written)
+ * token_table int32 [B, max_tokens]; entries < seq_lens[b] must be valid
+ *             slots; an out-of-range slot makes that sequence's output NaN
+ *             (nothing outside the pool is read)
+ * seq_lens    int32 [B], 0 <= seq_lens[b] <= max_tokens (clamped); a
+ *             zero-length sequence yields a zero output and lse = -inf
+ * out, lse, dtype, D, scale, workspace and errors as for ks_paged_decode.
+ */
+size_t ks_paged_decode_bs1_workspace(int B, int Hq, int D, int max_tokens);
+ks_status ks_paged_decode_bs1(const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* token_table,
+                              const int32_t* seq_lens, void* out, float* lse,
+                              int B, int Hq, int Hkv, int D, int max_tokens,
+                              int num_pool_tokens, int dtype, float scale,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ks_append_kv_bs1 -- ks_append_kv with single-token blocks: the new token's
+ * rotated key and its value go to pool slot token_table[b][seq_lens[b] - 1].
+ *
+ * k_pool, v_pool [num_pool_tokens, Hkv, D] bf16; token_table int32
+ * [B, max_tokens]; other arguments, skips and errors as for ks_append_kv.
+ */
+ks_status ks_append_kv_bs1(const void* k_new, const void* v_new,
+                           const int32_t* pos, const int32_t* token_table,
+                           const int32_t* seq_lens, void* k_pool, void* v_pool,
+                           int B, int Hkv, int D, int max_tokens,
+                           int num_pool_tokens, int dtype, float base,
+                           void* stream);
 
 #ifdef __cplusplus
 }

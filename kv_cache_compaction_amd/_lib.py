@@ -47,6 +47,9 @@ _SIGS = {
     "ks_paged_decode_workspace": ([_i, _i, _i, _i], _sz),
     "ks_paged_decode": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
     "ks_append_kv": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _f, _vp], _i),
+    "ks_paged_decode_bs1_workspace": ([_i, _i, _i, _i], _sz),
+    "ks_paged_decode_bs1": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+    "ks_append_kv_bs1": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _f, _vp], _i),
 }
 
 _lib = None
@@ -299,3 +302,63 @@ def ks_append_kv(k_new, v_new, pos, table, seq_lens, k_pool, v_pool, base=10000.
                           _ptr(k_pool), _ptr(v_pool), B, Hkv, D, table.shape[1], NB,
                           _dtype_code(k_new), float(base), _stream(stream))
     _check("ks_append_kv", st)
+
+
+def ks_paged_decode_bs1_workspace(B, Hq, D, max_tokens):
+    return load_library().ks_paged_decode_bs1_workspace(B, Hq, D, max_tokens)
+
+
+def ks_paged_decode_bs1(q, k_pool, v_pool, token_table, seq_lens, scale=None, out=None,
+                        lse=None, ws=None, stream=None):
+    """One GQA decode step over single-token-block caches: pools
+    [slots, Hkv, D], token_table [B, max_tokens].  Returns (out, lse)."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    _need(k_pool.dim() == 3, "pool must be [slots, Hkv, D]")
+    NT, Hkv, _ = k_pool.shape
+    _cuda_contig("q", q)
+    _cuda_contig("k_pool", k_pool, q.dtype)
+    _cuda_contig("v_pool", v_pool, q.dtype)
+    _cuda_contig("token_table", token_table, torch.int32)
+    _cuda_contig("seq_lens", seq_lens, torch.int32)
+    _need(tuple(v_pool.shape) == tuple(k_pool.shape), "v_pool shape")
+    _need(token_table.shape[0] == B and tuple(seq_lens.shape) == (B,),
+          "token_table/seq_lens shape")
+    MT = token_table.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    nbytes = lib.ks_paged_decode_bs1_workspace(B, Hq, D, max(MT, 1))
+    ws = _workspace(nbytes, q.device, ws)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.ks_paged_decode_bs1(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(token_table),
+                                 _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, MT, NT,
+                                 _dtype_code(q), sc, _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream))
+    _check("ks_paged_decode_bs1", st)
+    return out, lse
+
+
+def ks_append_kv_bs1(k_new, v_new, pos, token_table, seq_lens, k_pool, v_pool, base=10000.0,
+                     stream=None):
+    """Rotate k_new [B, Hkv, D] at pos [B] and write it and v_new into slot
+    token_table[b, seq_lens[b] - 1] of the single-token-block pools."""
+    lib = load_library()
+    B, Hkv, D = k_new.shape
+    NT = k_pool.shape[0]
+    _cuda_contig("k_new", k_new)
+    _cuda_contig("v_new", v_new, k_new.dtype)
+    _cuda_contig("k_pool", k_pool, k_new.dtype)
+    _cuda_contig("v_pool", v_pool, k_new.dtype)
+    _cuda_contig("pos", pos, torch.int32)
+    _cuda_contig("token_table", token_table, torch.int32)
+    _cuda_contig("seq_lens", seq_lens, torch.int32)
+    _need(tuple(v_new.shape) == (B, Hkv, D), "v_new shape")
+    _need(tuple(k_pool.shape) == (NT, Hkv, D) and v_pool.shape == k_pool.shape, "pool shape")
+    _need(tuple(pos.shape) == (B,) and tuple(seq_lens.shape) == (B,)
+          and token_table.shape[0] == B, "pos/seq_lens/token_table shape")
+    st = lib.ks_append_kv_bs1(_ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(token_table),
+                              _ptr(seq_lens), _ptr(k_pool), _ptr(v_pool), B, Hkv, D,
+                              token_table.shape[1], NT, _dtype_code(k_new), float(base),
+                              _stream(stream))
+    _check("ks_append_kv_bs1", st)

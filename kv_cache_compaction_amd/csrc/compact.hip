@@ -4,9 +4,9 @@
 // table: no empty slots may remain, so whole blocks are removed and the rest
 // concatenated).
 //
-// One workgroup per sequence.  Each pass covers 4 entries per thread
-// (1024 threads -> 4096 entries, one pass for every table up to 4096
-// blocks).  Within a pass: a wave-wide ballot + mbcnt gives each thread its
+// One workgroup per sequence for rows of up to 4096 entries (4 entries per
+// thread, 1024 threads: one pass); longer rows get one workgroup per
+// 4096-entry chunk (below).  Within a pass: a wave-wide ballot + mbcnt gives each thread its
 // rank among the kept entries of its wave, wave totals are scanned in LDS,
 // and kept entries are scattered to base + rank.  Tables are int32 and the
 // whole row is touched once, so the kernel is bandwidth/latency bound.
@@ -211,6 +211,322 @@ __global__ __launch_bounds__(kThreads) void compact_rounds_kernel(
   if (tid == 0) nout[b] = n;
 }
 
+// ---------------------------------------------------------------------------
+// Rows longer than one pass (token tables of single-token blocks reach tens
+// of thousands of entries): one workgroup per 4096-entry chunk, so a long
+// row is spread over the chip instead of looping in one workgroup.  Each
+// workgroup counts the kept entries before its chunk and in the whole row
+// from the keep flags (one byte per entry, read by every chunk of the row
+// and so served from L2), then compacts its own chunk at that offset and
+// fills the part of [kept, MB) that falls in its chunk with -1.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// kept entries among [0, n) of a keep row: all of them, and those before c0
+// (both summed over the workgroup; every thread gets the sums)
+__device__ __forceinline__ void count_kept(const uint8_t* __restrict__ kr, int n, int c0,
+                                           int* red, int& before, int& all) {
+  const int tid = threadIdx.x, w = tid >> 6;
+  int cb = 0, ca = 0;
+  for (int k = tid * kPer; k < n; k += kThreads * kPer) {
+    int f[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) f[u] = kr[min(k + u, n - 1)] != 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int ok = (k + u < n) & f[u];
+      ca += ok;
+      cb += (k + u < c0) ? ok : 0;
+    }
+  }
+  cb = wave_sum(cb);
+  ca = wave_sum(ca);
+  if ((tid & 63) == 0) {
+    red[w] = cb;
+    red[kWaves + w] = ca;
+  }
+  __syncthreads();
+  before = 0;
+  all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    before += red[i];
+    all += red[kWaves + i];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void compact_chunk_kernel(
+    const int32_t* __restrict__ tin, const int32_t* __restrict__ nin,
+    const uint8_t* __restrict__ keep, int32_t* __restrict__ tout,
+    int32_t* __restrict__ nout, const int32_t* __restrict__ pin,
+    int32_t* __restrict__ pout, int MB, int write_n) {
+  __shared__ int wsum[kWaves];
+  __shared__ int red[2 * kWaves];
+  const int c = blockIdx.x, b = blockIdx.y;
+  const size_t row = static_cast<size_t>(b) * MB;
+  int n = nin[b];
+  n = n < 0 ? 0 : (n > MB ? MB : n);
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int c0 = c * kRoundBlocks;
+  const int k0 = c0 + tid * kPer;
+  // this chunk's entries: the addresses do not depend on the counts
+  int kp[kPer], vals[kPer], poss[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int k = min(k0 + u, MB - 1);
+    kp[u] = keep[row + k];
+    vals[u] = tin[row + k];
+    poss[u] = pin ? pin[row + k] : 0;
+  }
+  int before, all;
+  count_kept(keep + row, n, c0, red, before, all);
+  int flags[kPer];
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    flags[u] = k0 + u < n && kp[u] != 0;
+    cnt += flags[u];
+  }
+  int pre = 0, tot_w = 0;
+#pragma unroll
+  for (int bit = 0; bit < 3; ++bit) {
+    const uint64_t m = __ballot((cnt >> bit) & 1);
+    pre += lane_rank(m) << bit;
+    tot_w += __popcll(m) << bit;
+  }
+  if ((tid & 63) == 0) wsum[w] = tot_w;
+  __syncthreads();
+  int off = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) off += (i < w) ? wsum[i] : 0;
+  int dst = before + off + pre;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if (flags[u]) {
+      tout[row + dst] = vals[u];
+      if (pout) pout[row + dst] = poss[u];
+      ++dst;
+    }
+  }
+  const int c1 = min(c0 + kRoundBlocks, MB);
+  for (int k = max(c0, all) + tid; k < c1; k += kThreads) {
+    tout[row + k] = -1;
+    if (pout) pout[row + k] = -1;
+  }
+  if (write_n && c == 0 && tid == 0) nout[b] = all;
+}
+
+// lengths after compaction, for the case nblk_out aliases nblk_in (the chunk
+// kernel's workgroups all read nblk_in, so none of them may overwrite it)
+__global__ __launch_bounds__(kThreads) void count_kept_kernel(
+    const int32_t* __restrict__ nin, const uint8_t* __restrict__ keep,
+    int32_t* __restrict__ nout, int MB) {
+  __shared__ int red[2 * kWaves];
+  const int b = blockIdx.x;
+  int n = nin[b];
+  n = n < 0 ? 0 : (n > MB ? MB : n);
+  int before, all;
+  count_kept(keep + static_cast<size_t>(b) * MB, n, 0, red, before, all);
+  if (threadIdx.x == 0) nout[b] = all;
+}
+
+// ---------------------------------------------------------------------------
+// Several events on rows longer than 4096 entries (token tables): the row
+// does not fit on chip, but which of its entries survive does.  Thread t
+// owns entries t + 1024 i (i < 64) and keeps one "alive" bit per entry.  Per
+// event, the rank of every alive entry in the current table is its position
+// in the (i, wave, lane) order among alive entries: wave ballots give counts
+// per (i, wave) cell, one workgroup scan over the 1024 cells gives their
+// offsets, and mbcnt the rank within the cell.  The event's keep flag of
+// that rank then decides the bit; each event's flag row is staged in LDS
+// while the previous event is processed.  After the last event the same
+// ranks are the output positions, and the table row is read once.
+// ---------------------------------------------------------------------------
+constexpr int kLongBits = 64;                        // entries per thread
+constexpr int kLongMax = kThreads * kLongBits;       // 65536 entries
+
+// Cell (i, w) is stored at cell[w * 64 + i] (a wave's cells contiguous) but
+// scanned in (i, w) order, the order of the entries t + 1024 i.
+__device__ __forceinline__ int cell_at(int i, int w) { return w * kLongBits + i; }
+
+// exclusive prefix over the cells in (i, w) order, in place; returns the
+// total (every thread)
+__device__ __forceinline__ int cell_scan(int* cell, int* wtot) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int at = cell_at(tid / kWaves, tid % kWaves);     // thread = cell in scan order
+  const int v = cell[at];
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    x += lane >= o ? y : 0;
+  }
+  if (lane == 63) wtot[w] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int sw = wtot[i];
+    off += i < w ? sw : 0;
+    tot += sw;
+  }
+  cell[at] = off + x - v;
+  __syncthreads();
+  return tot;
+}
+
+// counts of alive entries per (i, wave) cell
+// (lane i of each wave holds the count of its cell i)
+__device__ __forceinline__ void cell_counts(uint64_t alive, int* cell) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int mine = 0;
+  // partly unrolled on purpose: fully unrolled, the 64 loop-invariant lane
+  // compares are hoisted into scalar registers and spilled
+#pragma unroll 4
+  for (int i = 0; i < kLongBits; ++i) {
+    const int c = __popcll(__ballot((alive >> i) & 1));
+    mine = lane == i ? c : mine;
+  }
+  cell[cell_at(lane, w)] = mine;
+  __syncthreads();
+}
+
+// One event's keep row staged in LDS: the aligned 16-byte chunks that hold
+// the row's MB bytes (each chunk holds at least one byte of the row, so no
+// load leaves the pages the row lives on); byte k of the row is at
+// [delta + k].  Loads are issued into registers first (kStageRegs chunks
+// per thread) so that they fly while the previous event is processed.
+constexpr int kStageRegs = (kLongMax / 16 + 1 + kThreads - 1) / kThreads;   // 5
+constexpr int kStageBytes = (kLongMax / 16 + 1) * 16;   // chunks of one row, at most
+
+struct KeepStage {
+  u32x4 v[kStageRegs];
+  int delta;
+  int nchunk;
+};
+
+__device__ __forceinline__ void stage_issue(const uint8_t* kr, int MB, KeepStage& st) {
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(kr);
+  const uintptr_t a0 = addr & ~static_cast<uintptr_t>(15);
+  st.delta = static_cast<int>(addr - a0);
+  st.nchunk = static_cast<int>((addr + MB - a0 + 15) >> 4);
+  const u32x4* src = reinterpret_cast<const u32x4*>(a0);
+#pragma unroll
+  for (int u = 0; u < kStageRegs; ++u) {
+    const int c = threadIdx.x + u * kThreads;
+    if (c < st.nchunk) st.v[u] = src[c];
+  }
+}
+
+__device__ __forceinline__ void stage_store(const KeepStage& st, uint8_t* buf) {
+#pragma unroll
+  for (int u = 0; u < kStageRegs; ++u) {
+    const int c = threadIdx.x + u * kThreads;
+    if (c < st.nchunk) reinterpret_cast<u32x4*>(buf)[c] = st.v[u];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void compact_rounds_long_kernel(
+    const int32_t* __restrict__ tin, const int32_t* __restrict__ nin,
+    const uint8_t* __restrict__ keep, int rounds, int32_t* __restrict__ tout,
+    int32_t* __restrict__ nout, const int32_t* __restrict__ pin,
+    int32_t* __restrict__ pout, int B, int MB) {
+  __shared__ __attribute__((aligned(16))) int cell[kThreads];
+  __shared__ int wtot[kWaves];
+  __shared__ __attribute__((aligned(16))) uint8_t kst[2][kStageBytes];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const size_t row = static_cast<size_t>(b) * MB;
+  const size_t rstride = static_cast<size_t>(B) * MB;
+  int n = nin[b];
+  n = n < 0 ? 0 : (n > MB ? MB : n);
+  uint64_t alive = 0;
+#pragma unroll
+  for (int i = 0; i < kLongBits; ++i)
+    alive |= static_cast<uint64_t>(tid + kThreads * i < n) << i;
+
+  KeepStage st;
+  if (rounds > 0) {
+    stage_issue(keep + row, MB, st);
+    stage_store(st, kst[0]);
+  }
+  for (int r = 0; r < rounds; ++r) {
+    const int delta = st.delta;
+    const uint8_t* kl = kst[r & 1] + delta;
+    // next event's flags: in flight while this one is processed
+    if (r + 1 < rounds) stage_issue(keep + (r + 1) * rstride + row, MB, st);
+    cell_counts(alive, cell);      // its barrier also publishes kst[r & 1]
+    cell_scan(cell, wtot);
+    // branch-free: every lane reads a flag (a lane that is not alive reads
+    // byte <= the event's length, inside the staged row) and masks it
+    uint64_t next = 0;
+#pragma unroll 1
+    for (int i0 = 0; i0 < kLongBits; i0 += 16) {
+      int rk[16];
+      const int4* cw = reinterpret_cast<const int4*>(cell + cell_at(i0, w));
+      const int4 c4[4] = {cw[0], cw[1], cw[2], cw[3]};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint64_t m = __ballot((alive >> (i0 + j)) & 1);
+        const int4 c = c4[j / 4];
+        const int cj = (j % 4 == 0) ? c.x : (j % 4 == 1) ? c.y : (j % 4 == 2) ? c.z : c.w;
+        rk[j] = cj + lane_rank(m);
+      }
+      int fl[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) fl[j] = kl[rk[j]];
+      // keep the 16 gathers in flight together (left alone, the scheduler
+      // waits for each one before issuing the next)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint64_t f = fl[j] != 0;
+        next |= (f & (alive >> (i0 + j))) << (i0 + j);
+      }
+    }
+    alive = next;
+    if (r + 1 < rounds) stage_store(st, kst[(r + 1) & 1]);
+    __syncthreads();  // cell is rewritten by the next event
+  }
+
+  cell_counts(alive, cell);
+  const int total = cell_scan(cell, wtot);
+  // 16 entries per batch: loads (clamped into the row) all in flight, then
+  // the stores of the alive ones
+#pragma unroll 1
+  for (int i0 = 0; i0 < kLongBits; i0 += 16) {
+    int dst[16], v[16], pv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool a = (alive >> (i0 + j)) & 1;
+      const uint64_t m = __ballot(a);
+      dst[j] = a ? cell[cell_at(i0 + j, w)] + lane_rank(m) : -1;
+      const size_t src = row + min(tid + kThreads * (i0 + j), MB - 1);
+      v[j] = tin[src];
+      pv[j] = pin ? pin[src] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (dst[j] >= 0) {
+        tout[row + dst[j]] = v[j];
+        if (pout) pout[row + dst[j]] = pv[j];
+      }
+    }
+  }
+  for (int k = total + tid; k < MB; k += kThreads) {
+    tout[row + k] = -1;
+    if (pout) pout[row + k] = -1;
+  }
+  if (tid == 0) nout[b] = total;
+}
+
 }  // namespace
 
 extern "C" ks_status ks_compact_block_table(const int32_t* table_in, const int32_t* nblk_in,
@@ -238,10 +554,24 @@ extern "C" ks_status ks_compact_block_table(const int32_t* table_in, const int32
                    !overlap(pos_out, table_in),
                "ks_compact_block_table: pos_out must not alias the other tables");
   }
-  hipLaunchKernelGGL(compact_kernel, dim3(B), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), table_in, nblk_in, keep, table_out,
-                     nblk_out, pos_in, pos_out, max_blocks);
-  return ks_check_launch("ks_compact_block_table");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_blocks <= kRoundBlocks) {
+    hipLaunchKernelGGL(compact_kernel, dim3(B), dim3(kThreads), 0, s, table_in, nblk_in, keep,
+                       table_out, nblk_out, pos_in, pos_out, max_blocks);
+    return ks_check_launch("ks_compact_block_table");
+  }
+  KS_REQUIRE(B < 65536, "ks_compact_block_table: B=%d too large for rows above %d entries", B,
+             kRoundBlocks);
+  const int nchunks = (max_blocks + kRoundBlocks - 1) / kRoundBlocks;
+  const bool n_alias = nblk_in == nblk_out;
+  hipLaunchKernelGGL(compact_chunk_kernel, dim3(nchunks, B), dim3(kThreads), 0, s, table_in,
+                     nblk_in, keep, table_out, nblk_out, pos_in, pos_out, max_blocks,
+                     n_alias ? 0 : 1);
+  ks_status st = ks_check_launch("ks_compact_block_table");
+  if (st != KS_OK || !n_alias) return st;
+  hipLaunchKernelGGL(count_kept_kernel, dim3(B), dim3(kThreads), 0, s, nblk_in, keep, nblk_out,
+                     max_blocks);
+  return ks_check_launch("ks_compact_block_table(count)");
 }
 
 extern "C" ks_status ks_compact_block_table_rounds(const int32_t* table_in,
@@ -281,8 +611,14 @@ extern "C" ks_status ks_compact_block_table_rounds(const int32_t* table_in,
                        nblk_out, pos_in, pos_out, max_blocks);
     return ks_check_launch("ks_compact_block_table_rounds");
   }
-  hipLaunchKernelGGL(compact_rounds_kernel, dim3(B), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), table_in, nblk_in, keep, rounds,
-                     table_out, nblk_out, pos_in, pos_out, B, max_blocks);
+  static_assert(kLongMax == KS_MAX_ROUND_BLOCKS, "round limit");
+  if (max_blocks <= kRoundBlocks)
+    hipLaunchKernelGGL(compact_rounds_kernel, dim3(B), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), table_in, nblk_in, keep, rounds,
+                       table_out, nblk_out, pos_in, pos_out, B, max_blocks);
+  else
+    hipLaunchKernelGGL(compact_rounds_long_kernel, dim3(B), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), table_in, nblk_in, keep, rounds,
+                       table_out, nblk_out, pos_in, pos_out, B, max_blocks);
   return ks_check_launch("ks_compact_block_table_rounds");
 }

@@ -26,6 +26,14 @@
 //   * At the end the 16 token slots are merged with DPP row rotations.
 // Kernel 2 (reduce): merges the splits of each (sequence, head).
 //
+// Single-token blocks (BS = 1, the SGLang setup: explainer, paragraph on
+// padding completions to whole blocks): the table lists one pool slot per
+// token and the pool is [slots, Hkv, D].  The same kernels run over groups
+// of 16 consecutive table entries; the split's 768 slot ids are staged in LDS
+// once and lane (t, g) reads the id of its own token slot t of each group, so
+// every load instruction still covers 64 contiguous bytes of 16 token rows
+// (now 16 separate rows of the pool).
+//
 // Memory: K and V of every live token are read exactly once per step; the
 // split partials add 4(D+2) bytes per (sequence, head, split).  The grid runs
 // head groups fastest, so the Hkv waves reading the slices of one pool block
@@ -36,7 +44,7 @@
 namespace {
 
 constexpr int D = 128;
-constexpr int kSplit = 48;     // blocks per split (the split's block ids fit one wave)
+constexpr int kSplit = 48;     // 16-token groups per split (block ids fit one wave)
 static_assert(kSplit <= 64, "one block id per lane");
 constexpr float kTau = 8.0f;   // lazy-rescale slack, log2 units
 
@@ -66,21 +74,24 @@ struct BlockRegs {
   u32x4 v[4];
 };
 
-template <int HPW>
+// BS = tokens per pool block (16, or 1: one pool slot per token).  MB = table
+// entries per sequence, NB = pool blocks (slots when BS = 1).
+template <int HPW, int BS>
 __global__ __launch_bounds__(64) void decode_split_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kpool,
     const bf16_t* __restrict__ vpool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
     float* __restrict__ part_ml, int Hq, int Hkv, int MB, int NB, int nsplit_max,
     float sl2) {
+  static_assert(BS == 16 || BS == 1, "block size");
   const int hw = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int hq0 = hw * HPW;
   const int hkv = hq0 / G;
   // lengths beyond the table's capacity are clamped: nothing past a table
   // row is ever read
-  const int L = min(max(seq_lens[b], 0), 16 * MB);
-  const int nblk = (L + 15) >> 4;
+  const int L = min(max(seq_lens[b], 0), BS * MB);
+  const int nblk = (L + 15) >> 4;     // 16-token groups
   const int blk0 = split * kSplit;
   if (blk0 >= nblk) return;
   const int blk1 = min(nblk, blk0 + kSplit);
@@ -101,18 +112,35 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[h][i] = 0.f;
   }
-  // the split's block ids, one per lane, read once: block blk's id is then a
-  // wave-uniform value, and its K/V loads do not wait on a table load
   const int32_t* trow = table + static_cast<size_t>(b) * MB;
-  const int pids = lane < blk1 - blk0 ? trow[blk0 + lane] : 0;
   bool bad = false;
-  const size_t lane_off = static_cast<size_t>(t) * D + g * 8;
+  // BS = 16: the split's block ids, one per lane, read once; block blk's id
+  // is then a wave-uniform value and its K/V loads do not wait on a table
+  // load.  BS = 1: the split's slot ids (16 per group) staged in LDS.
+  int pids = 0;
+  __shared__ int sid[BS == 1 ? kSplit * 16 : 1];
+  if constexpr (BS == 16) {
+    pids = lane < blk1 - blk0 ? trow[blk0 + lane] : 0;
+  } else {
+    constexpr int kPerLane = kSplit * 16 / 64;
+    int v[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int tok = blk0 * 16 + i * 64 + lane;
+      v[i] = tok < L ? trow[tok] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) sid[i * 64 + lane] = v[i];
+    __syncthreads();
+  }
+  const size_t lane_off = static_cast<size_t>(BS == 16 ? t : 0) * D + g * 8;
 
   auto load = [&](int blk, BlockRegs& r) {
-    const int pid = __builtin_amdgcn_readlane(pids, blk - blk0);
+    const int pid = BS == 16 ? __builtin_amdgcn_readlane(pids, blk - blk0)
+                             : sid[(blk - blk0) * 16 + t];
     const bool ok = static_cast<unsigned>(pid) < static_cast<unsigned>(NB);
     bad |= !ok;
-    const size_t off = (static_cast<size_t>(ok ? pid : 0) * Hkv + hkv) * 16 * D + lane_off;
+    const size_t off = (static_cast<size_t>(ok ? pid : 0) * Hkv + hkv) * BS * D + lane_off;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       r.k[s] = *reinterpret_cast<const u32x4*>(kpool + off + s * 32);
@@ -178,6 +206,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   }
   if (blk < blk1) compute(blk, r0);
 
+  // with single-token blocks a bad slot id is seen by one lane only
+  if (BS == 1) bad = __ballot(bad) != 0;
   // merge the 16 token slots of each lane row (lanes with equal g)
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
@@ -204,12 +234,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   }
 }
 
+// cap = tokens one table row can reach (BS * entries)
 __global__ __launch_bounds__(D) void decode_reduce_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, bf16_t* __restrict__ out, float* __restrict__ lse,
-    int Hq, int MB, int nsplit_max) {
+    int Hq, int cap, int nsplit_max) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int L = min(max(seq_lens[b], 0), 16 * MB);
+  const int L = min(max(seq_lens[b], 0), cap);
   const int ns = (((L + 15) >> 4) + kSplit - 1) / kSplit;
   const size_t slot0 = (static_cast<size_t>(b) * Hq + h) * nsplit_max;
   float M = -INFINITY;
@@ -232,11 +263,12 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
 
 // ---------------------------------------------------------------------------
 // append: rotate the new token's key at its logical position and write key
-// and value into pool slot seq_len - 1 (block table entry (seq_len - 1) / 16).
+// and value into token slot seq_len - 1 (block table entry (seq_len - 1) / BS).
 // Keys are stored already rotated, so later compaction can move blocks
 // without touching their contents (explainer, RoPE paragraph).  One
 // workgroup per sequence; angles in fp64 as in ks_rope_logical.
 // ---------------------------------------------------------------------------
+template <int BS>
 __global__ __launch_bounds__(256) void append_kernel(
     const bf16_t* __restrict__ k_new, const bf16_t* __restrict__ v_new,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ table,
@@ -244,10 +276,10 @@ __global__ __launch_bounds__(256) void append_kernel(
     bf16_t* __restrict__ vpool, int Hkv, int MB, int NB, double log2_base) {
   __shared__ float2 cs[D / 2];
   const int b = blockIdx.x;
-  const int L = min(seq_lens[b], 16 * MB);
+  const int L = min(seq_lens[b], BS * MB);
   if (L < 1) return;
   const int slot = L - 1;
-  const int pid = table[static_cast<size_t>(b) * MB + (slot >> 4)];
+  const int pid = table[static_cast<size_t>(b) * MB + slot / BS];
   if (static_cast<unsigned>(pid) >= static_cast<unsigned>(NB)) return;
   for (int kk = threadIdx.x; kk < D / 2; kk += blockDim.x) {
     const double inv_freq = exp2(-2.0 * kk / D * log2_base);
@@ -260,7 +292,7 @@ __global__ __launch_bounds__(256) void append_kernel(
   for (int idx = threadIdx.x; idx < Hkv * (D / 16); idx += blockDim.x) {
     const int h = idx / (D / 16), ch = idx % (D / 16);
     const size_t src = (static_cast<size_t>(b) * Hkv + h) * D + ch * 8;
-    const size_t dst = ((static_cast<size_t>(pid) * Hkv + h) * 16 + (slot & 15)) * D + ch * 8;
+    const size_t dst = ((static_cast<size_t>(pid) * Hkv + h) * BS + slot % BS) * D + ch * 8;
     const u32x4 a = *reinterpret_cast<const u32x4*>(k_new + src);
     const u32x4 bb = *reinterpret_cast<const u32x4*>(k_new + src + D / 2);
     u32x4 ra, rb;
@@ -280,41 +312,42 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
 }
 
-inline int nsplit_for(int max_blocks) { return (max_blocks + kSplit - 1) / kSplit; }
+// splits for a table row of `groups` 16-token groups
+inline int nsplit_for(int groups) { return (groups + kSplit - 1) / kSplit; }
 
-}  // namespace
-
-extern "C" size_t ks_paged_decode_workspace(int B, int Hq, int Dh, int max_blocks) {
-  if (B <= 0 || Hq <= 0 || Dh <= 0 || max_blocks <= 0) return 0;
-  const size_t slots = static_cast<size_t>(B) * Hq * nsplit_for(max_blocks);
+inline size_t decode_workspace(int B, int Hq, int Dh, int groups) {
+  if (B <= 0 || Hq <= 0 || Dh <= 0 || groups <= 0) return 0;
+  const size_t slots = static_cast<size_t>(B) * Hq * nsplit_for(groups);
   return slots * (static_cast<size_t>(Dh) + 2) * sizeof(float) + 256;
 }
 
-extern "C" ks_status ks_paged_decode(const void* q, const void* k_pool, const void* v_pool,
-                                     const int32_t* table, const int32_t* seq_lens, void* out,
-                                     float* lse, int B, int Hq, int Hkv, int Dh, int max_blocks,
-                                     int num_pool_blocks, int dtype, float scale, void* ws,
-                                     size_t ws_bytes, void* stream) {
-  KS_REQUIRE(B >= 0 && Hq > 0 && Hkv > 0 && max_blocks >= 0 && num_pool_blocks >= 0,
-             "ks_paged_decode: bad sizes");
-  KS_REQUIRE(Hq % Hkv == 0, "ks_paged_decode: Hq %% Hkv != 0");
+template <int BS>
+ks_status decode_impl(const char* name, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* table, const int32_t* seq_lens, void* out, float* lse, int B,
+                      int Hq, int Hkv, int Dh, int max_entries, int num_pool, int dtype,
+                      float scale, void* ws, size_t ws_bytes, void* stream) {
+  KS_REQUIRE(B >= 0 && Hq > 0 && Hkv > 0 && max_entries >= 0 && num_pool >= 0,
+             "%s: bad sizes", name);
+  KS_REQUIRE(Hq % Hkv == 0, "%s: Hq %% Hkv != 0", name);
   if (dtype != KS_BF16 || Dh != D)
-    return ks_fail(KS_ERR_UNSUPPORTED, "ks_paged_decode: only bf16 with D=128 (got dtype=%d D=%d)",
+    return ks_fail(KS_ERR_UNSUPPORTED, "%s: only bf16 with D=128 (got dtype=%d D=%d)", name,
                    dtype, Dh);
   const int G = Hq / Hkv;
   const int hpw = G >= 4 ? 4 : G;
-  if (G % hpw != 0)
-    return ks_fail(KS_ERR_UNSUPPORTED, "ks_paged_decode: group size %d unsupported", G);
+  if (G % hpw != 0) return ks_fail(KS_ERR_UNSUPPORTED, "%s: group size %d unsupported", name, G);
   if (B == 0) return KS_OK;
-  KS_REQUIRE(q && k_pool && v_pool && table && seq_lens && out, "ks_paged_decode: null pointer");
+  KS_REQUIRE(q && k_pool && v_pool && table && seq_lens && out, "%s: null pointer", name);
   KS_REQUIRE(ks_aligned16(q) && ks_aligned16(k_pool) && ks_aligned16(v_pool) && ks_aligned16(out),
-             "ks_paged_decode: tensors must be 16-byte aligned");
-  // max_blocks == 0: every length clamps to 0 and no table entry is read
-  const size_t need = ks_paged_decode_workspace(B, Hq, Dh, max_blocks > 0 ? max_blocks : 1);
+             "%s: tensors must be 16-byte aligned", name);
+  KS_REQUIRE(static_cast<int64_t>(max_entries) * BS < (int64_t{1} << 31),
+             "%s: table row too long", name);
+  // max_entries == 0: every length clamps to 0 and no table entry is read
+  const int groups = max_entries > 0 ? (max_entries * BS + 15) / 16 : 1;
+  const size_t need = decode_workspace(B, Hq, Dh, groups);
   if (!ws || ws_bytes < need)
-    return ks_fail(KS_ERR_WORKSPACE, "ks_paged_decode: workspace %zu < %zu bytes", ws_bytes, need);
-  const int nsplit = max_blocks > 0 ? nsplit_for(max_blocks) : 1;
-  KS_REQUIRE(nsplit < 65536 && B < 65536, "ks_paged_decode: grid too large");
+    return ks_fail(KS_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
+  const int nsplit = nsplit_for(groups);
+  KS_REQUIRE(nsplit < 65536 && B < 65536, "%s: grid too large", name);
   float* part_ml = static_cast<float*>(ws);
   const size_t slots = static_cast<size_t>(B) * Hq * nsplit;
   float* part_o = reinterpret_cast<float*>(
@@ -328,40 +361,90 @@ extern "C" ks_status ks_paged_decode(const void* q, const void* k_pool, const vo
   const bf16_t* kp = static_cast<const bf16_t*>(k_pool);
   const bf16_t* vp = static_cast<const bf16_t*>(v_pool);
   if (hpw == 4)
-    hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(64), 0, s, qq, kp, vp, table, seq_lens,
-                       part_o, part_ml, Hq, Hkv, max_blocks, num_pool_blocks, nsplit, sl2);
+    hipLaunchKernelGGL((decode_split_kernel<4, BS>), grid, dim3(64), 0, s, qq, kp, vp, table,
+                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2);
   else if (hpw == 2)
-    hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(64), 0, s, qq, kp, vp, table, seq_lens,
-                       part_o, part_ml, Hq, Hkv, max_blocks, num_pool_blocks, nsplit, sl2);
+    hipLaunchKernelGGL((decode_split_kernel<2, BS>), grid, dim3(64), 0, s, qq, kp, vp, table,
+                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2);
   else
-    hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(64), 0, s, qq, kp, vp, table, seq_lens,
-                       part_o, part_ml, Hq, Hkv, max_blocks, num_pool_blocks, nsplit, sl2);
-  ks_status st = ks_check_launch("ks_paged_decode(split)");
+    hipLaunchKernelGGL((decode_split_kernel<1, BS>), grid, dim3(64), 0, s, qq, kp, vp, table,
+                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2);
+  ks_status st = ks_check_launch(name);
   if (st != KS_OK) return st;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(Hq, B), dim3(D), 0, s, part_o, part_ml, seq_lens,
-                     static_cast<bf16_t*>(out), lse, Hq, max_blocks, nsplit);
-  return ks_check_launch("ks_paged_decode(reduce)");
+                     static_cast<bf16_t*>(out), lse, Hq, max_entries * BS, nsplit);
+  return ks_check_launch(name);
+}
+
+template <int BS>
+ks_status append_impl(const char* name, const void* k_new, const void* v_new,
+                      const int32_t* pos, const int32_t* table, const int32_t* seq_lens,
+                      void* k_pool, void* v_pool, int B, int Hkv, int Dh, int max_entries,
+                      int num_pool, int dtype, float base, void* stream) {
+  KS_REQUIRE(B >= 0 && Hkv > 0 && max_entries >= 0 && num_pool >= 0, "%s: bad sizes", name);
+  KS_REQUIRE(base > 1.0f, "%s: base must be > 1", name);
+  if (dtype != KS_BF16 || Dh != D)
+    return ks_fail(KS_ERR_UNSUPPORTED, "%s: only bf16 with D=128 (dtype=%d D=%d)", name, dtype,
+                   Dh);
+  if (B == 0 || max_entries == 0) return KS_OK;
+  KS_REQUIRE(k_new && v_new && pos && table && seq_lens && k_pool && v_pool,
+             "%s: null pointer", name);
+  KS_REQUIRE(ks_aligned16(k_new) && ks_aligned16(v_new) && ks_aligned16(k_pool) &&
+                 ks_aligned16(v_pool),
+             "%s: tensors must be 16-byte aligned", name);
+  KS_REQUIRE(static_cast<int64_t>(max_entries) * BS < (int64_t{1} << 31),
+             "%s: table row too long", name);
+  hipLaunchKernelGGL(append_kernel<BS>, dim3(B), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new), pos,
+                     table, seq_lens, static_cast<bf16_t*>(k_pool), static_cast<bf16_t*>(v_pool),
+                     Hkv, max_entries, num_pool, log2(static_cast<double>(base)));
+  return ks_check_launch(name);
+}
+
+}  // namespace
+
+extern "C" size_t ks_paged_decode_workspace(int B, int Hq, int Dh, int max_blocks) {
+  return decode_workspace(B, Hq, Dh, max_blocks);
+}
+
+extern "C" ks_status ks_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* table, const int32_t* seq_lens, void* out,
+                                     float* lse, int B, int Hq, int Hkv, int Dh, int max_blocks,
+                                     int num_pool_blocks, int dtype, float scale, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return decode_impl<16>("ks_paged_decode", q, k_pool, v_pool, table, seq_lens, out, lse, B, Hq,
+                         Hkv, Dh, max_blocks, num_pool_blocks, dtype, scale, ws, ws_bytes,
+                         stream);
+}
+
+extern "C" size_t ks_paged_decode_bs1_workspace(int B, int Hq, int Dh, int max_tokens) {
+  if (max_tokens <= 0) return 0;
+  return decode_workspace(B, Hq, Dh, (max_tokens + 15) / 16);
+}
+
+extern "C" ks_status ks_paged_decode_bs1(const void* q, const void* k_pool, const void* v_pool,
+                                         const int32_t* token_table, const int32_t* seq_lens,
+                                         void* out, float* lse, int B, int Hq, int Hkv, int Dh,
+                                         int max_tokens, int num_pool_tokens, int dtype,
+                                         float scale, void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl<1>("ks_paged_decode_bs1", q, k_pool, v_pool, token_table, seq_lens, out,
+                        lse, B, Hq, Hkv, Dh, max_tokens, num_pool_tokens, dtype, scale, ws,
+                        ws_bytes, stream);
 }
 
 extern "C" ks_status ks_append_kv(const void* k_new, const void* v_new, const int32_t* pos,
                                   const int32_t* table, const int32_t* seq_lens, void* k_pool,
                                   void* v_pool, int B, int Hkv, int Dh, int max_blocks,
                                   int num_pool_blocks, int dtype, float base, void* stream) {
-  KS_REQUIRE(B >= 0 && Hkv > 0 && max_blocks >= 0 && num_pool_blocks >= 0,
-             "ks_append_kv: bad sizes");
-  KS_REQUIRE(base > 1.0f, "ks_append_kv: base must be > 1");
-  if (dtype != KS_BF16 || Dh != D)
-    return ks_fail(KS_ERR_UNSUPPORTED, "ks_append_kv: only bf16 with D=128 (dtype=%d D=%d)",
-                   dtype, Dh);
-  if (B == 0 || max_blocks == 0) return KS_OK;
-  KS_REQUIRE(k_new && v_new && pos && table && seq_lens && k_pool && v_pool,
-             "ks_append_kv: null pointer");
-  KS_REQUIRE(ks_aligned16(k_new) && ks_aligned16(v_new) && ks_aligned16(k_pool) &&
-                 ks_aligned16(v_pool),
-             "ks_append_kv: tensors must be 16-byte aligned");
-  hipLaunchKernelGGL(append_kernel, dim3(B), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new), pos,
-                     table, seq_lens, static_cast<bf16_t*>(k_pool), static_cast<bf16_t*>(v_pool),
-                     Hkv, max_blocks, num_pool_blocks, log2(static_cast<double>(base)));
-  return ks_check_launch("ks_append_kv");
+  return append_impl<16>("ks_append_kv", k_new, v_new, pos, table, seq_lens, k_pool, v_pool, B,
+                         Hkv, Dh, max_blocks, num_pool_blocks, dtype, base, stream);
+}
+
+extern "C" ks_status ks_append_kv_bs1(const void* k_new, const void* v_new, const int32_t* pos,
+                                      const int32_t* token_table, const int32_t* seq_lens,
+                                      void* k_pool, void* v_pool, int B, int Hkv, int Dh,
+                                      int max_tokens, int num_pool_tokens, int dtype, float base,
+                                      void* stream) {
+  return append_impl<1>("ks_append_kv_bs1", k_new, v_new, pos, token_table, seq_lens, k_pool,
+                        v_pool, B, Hkv, Dh, max_tokens, num_pool_tokens, dtype, base, stream);
 }

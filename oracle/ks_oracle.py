@@ -243,19 +243,23 @@ def paged_decode(q, k_pool, v_pool, table, seq_lens, scale=None):
     """One decode step over paged caches.
 
     q [B, Hq, D] (already rotated at its logical position); k_pool, v_pool
-    [NB, Hkv, 16, D] (keys stored rotated at their own logical positions);
+    [NB, Hkv, BS, D] (keys stored rotated at their own logical positions);
     table [B, MB]; seq_lens [B].  Sequence b attends the first seq_lens[b]
     tokens reached through its table.  Returns (out [B, Hq, D], lse [B, Hq]).
+
+    The block size BS is the pool's third axis: 16 for the vLLM setup, 1 for
+    SGLang's single-token blocks, whose table lists one pool slot per token
+    (explainer, paragraph on padding completions to whole blocks).
     """
     B, Hq, D = q.shape
-    Hkv = k_pool.shape[1]
+    Hkv, BS = k_pool.shape[1], k_pool.shape[2]
     G = Hq // Hkv
     sc = _scale(D, scale)
     out = np.zeros((B, Hq, D))
     lse = np.zeros((B, Hq))
     for b in range(B):
         L = int(seq_lens[b])
-        nb = (L + BLOCK - 1) // BLOCK
+        nb = (L + BS - 1) // BS
         blocks = [int(table[b][x]) for x in range(nb)]
         for kv in range(Hkv):
             keys = np.concatenate([np.asarray(k_pool[p, kv], dtype=np.float64)

@@ -110,7 +110,7 @@ def test_compaction_rounds_argument_checks(lib):
                       ctypes.c_void_p(1 << 20), None, None, 4, 32, None)
     assert st == 1 and "rounds" in msg
     st, msg = _status(lib, "ks_compact_block_table_rounds", FAKE, FAKE, FAKE, 2, FAKE,
-                      ctypes.c_void_p(1 << 20), None, None, 4, 4097, None)
+                      ctypes.c_void_p(1 << 20), None, None, 4, 65537, None)
     assert st == 1 and "max_blocks" in msg
     st, msg = _status(lib, "ks_compact_block_table_rounds", FAKE, FAKE, FAKE, 2, FAKE, FAKE,
                       None, None, 4, 32, None)
@@ -118,3 +118,22 @@ def test_compaction_rounds_argument_checks(lib):
     st, _ = _status(lib, "ks_compact_block_table_rounds", None, None, None, 3, None, None, None,
                     None, 0, 32, None)
     assert st == 0  # B == 0 is a no-op
+
+
+def test_single_token_block_argument_checks(lib):
+    st, _ = _status(lib, "ks_paged_decode_bs1", *([FAKE] * 7), 2, 32, 8, 64, 10, 100, 1, 0.1,
+                    FAKE, 1 << 20, None)
+    assert st == 2  # D = 64 not provided
+    need = lib.ks_paged_decode_bs1_workspace(64, 32, 128, 65537)
+    assert need == lib.ks_paged_decode_workspace(64, 32, 128, 4097)
+    st, _ = _status(lib, "ks_paged_decode_bs1", *([FAKE] * 7), 64, 32, 8, 128, 65537, 10, 1,
+                    0.1, FAKE, need - 1, None)
+    assert st == 4
+    st, msg = _status(lib, "ks_paged_decode_bs1", *([FAKE] * 7), 4, 32, 6, 128, 100, 10, 1, 0.1,
+                      FAKE, 1 << 20, None)
+    assert st == 1 and "Hq" in msg
+    st, _ = _status(lib, "ks_append_kv_bs1", *([FAKE] * 7), 2, 8, 128, 10, 100, 1, 0.5, None)
+    assert st == 1  # base must exceed 1
+    st, _ = _status(lib, "ks_append_kv_bs1", *([FAKE] * 7), 0, 8, 128, 10, 100, 1, 10000.0,
+                    None)
+    assert st == 0

@@ -442,3 +442,72 @@ def test_decode_batch_structure():
         assert 1 <= len(db.runs[b]) <= 6
         for (x0, x1) in db.runs[b]:
             assert x0 >= 1 and x1 <= db.nblk0[b] - 2
+
+
+# ---------------------------------------------------------------------------
+# Single-token blocks (token-granular traces, tables and decode)
+# ---------------------------------------------------------------------------
+def test_token_granular_trace_decode_and_compaction():
+    """With single-token blocks nothing is padded: turns end anywhere, the
+    token table of the final live set is the splice of the per-token keep
+    flags, and decode over it equals row T of the masked trace attention."""
+    rng = np.random.default_rng(150)
+    tr = build_trace(rng, 777, 37, 400, "recent", turn_len=(23, 97), granule=1)
+    check_trace(tr)
+    assert any(x % 16 for (x, _) in tr.turns)          # really unpadded
+    N, Hq, Hkv, D = tr.N, 4, 2, 16
+    T = N - 1
+    qr, kr, v = rnd((1, N, Hq, D), 151), rnd((1, N, Hkv, D), 152), rnd((1, N, Hkv, D), 153)
+    pos = np.arange(N)[None]
+    q, k = O.rope(qr, pos), O.rope(kr, pos)
+    e = tr.e[None].astype(np.int64)
+    # token table before compaction: a permutation of pool slots
+    NT = N + 5
+    slots = rng.permutation(NT)[:N]
+    kp = np.full((NT, Hkv, 1, D), np.nan)
+    vp = np.full((NT, Hkv, 1, D), np.nan)
+    kp[slots, :, 0], vp[slots, :, 0] = k[0], v[0]
+    keep = (tr.e == KS_NEVER).astype(np.uint8)[None]
+    table, n = O.compact_block_table(slots[None].astype(np.int32), np.array([N]), keep)
+    live = O.live_keys(e[0], T)
+    assert int(n[0]) == len(live)
+    np.testing.assert_array_equal(table[0, :n[0]], slots[live])
+    out, lse = O.paged_decode(q[:, T], kp, vp, table, n)
+    for h in range(Hq):
+        oh, lh = O.attn_fwd_rows(q, k, v, e, 0, h, np.array([T]))
+        np.testing.assert_allclose(out[0, h], oh[0], atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], lh[0], atol=1e-12)
+
+
+def test_decode_single_token_blocks_equal_16_token_blocks():
+    """The same live tokens reached through 16-token blocks or through one
+    slot per token give the same decode (the layout is not the math)."""
+    rng = np.random.default_rng(160)
+    L, Hq, Hkv, D = 83, 4, 1, 16
+    kr, v = rnd((L, Hkv, D), 161), rnd((L, Hkv, D), 162)
+    q = rnd((1, Hq, D), 163)
+    kp16, vp16, blocks = _pool_from_trace(kr, v, list(range(L)), rng)
+    slots = rng.permutation(L + 9)[:L]
+    kp1 = np.full((L + 9, Hkv, 1, D), np.nan)
+    vp1 = np.full((L + 9, Hkv, 1, D), np.nan)
+    kp1[slots, :, 0], vp1[slots, :, 0] = kr, v
+    o16, l16 = O.paged_decode(q, kp16, vp16, np.array([list(blocks)]), np.array([L]))
+    o1, l1 = O.paged_decode(q, kp1, vp1, slots[None], np.array([L]))
+    np.testing.assert_allclose(o1, o16, atol=1e-13)
+    np.testing.assert_allclose(l1, l16, atol=1e-13)
+    ref = _sdpa(q[0], kr[:, 0], v[:, 0])          # every head sees all L keys
+    np.testing.assert_allclose(o1[0], ref, atol=1e-12)
+
+
+def test_token_decode_batch_structure():
+    db = build_decode_batch(np.random.default_rng(1004), 64, block=1)
+    assert db.block == 1 and np.any(db.live_len % 16) and np.any(db.pos % 16)
+    assert db.live_len.min() >= 4096 and db.live_len.max() <= 16384
+    ids = np.concatenate([db.table0[b, :db.nblk0[b]] for b in range(64)])
+    assert len(np.unique(ids)) == len(ids) == db.num_pool_blocks
+    # replaying the rounds leaves exactly L_b + 1 slots (live tokens + the
+    # decoded token's slot)
+    out, n = db.table0, db.nblk0
+    for r in range(db.keeps.shape[0]):
+        out, n = O.compact_block_table(out, n, db.keeps[r])
+    np.testing.assert_array_equal(n, db.live_len + 1)

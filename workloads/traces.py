@@ -29,8 +29,8 @@ KS_NEVER = 2**31 - 1      # e_j of a token that is never evicted
 BLOCK = 16                # tokens per KV block
 
 
-def _round_up16(x: int) -> int:
-    return (int(x) + 15) // 16 * 16
+def _round_up(x: int, g: int) -> int:
+    return (int(x) + g - 1) // g * g
 
 
 @dataclass
@@ -54,16 +54,20 @@ class Trace:
     live_units: list = field(default_factory=list)  # live spans after the trace
     overlap: int = 0
     summary: int = 0
+    granule: int = BLOCK             # turn lengths are multiples of this
 
 
 def build_trace(rng: np.random.Generator, N: int, P: int, budget: int,
                 strategy: str, turn_len=(64, 512), overlap: int = 0,
-                summary: int = 0) -> Trace:
+                summary: int = 0, granule: int = BLOCK) -> Trace:
     """Build one trace.
 
     Turn lengths are integers uniform on ``turn_len`` (inclusive), rounded up
-    to a multiple of 16; a fixed length is given as ``turn_len=(L, L)``.  The
-    last turn is cut at ``N``.
+    to a multiple of ``granule``; a fixed length is given as
+    ``turn_len=(L, L)``.  The last turn is cut at ``N``.  ``granule`` 16 is
+    the vLLM setup, whose completions are padded to whole 16-token blocks;
+    ``granule`` 1 is the SGLang setup with single-token blocks and no padding
+    (explainer, paragraph on turns ending inside a block).
 
     Trigger: at the end of a turn, if the live size plus the next turn's
     length would exceed ``budget``, an event fires at that turn end.
@@ -81,7 +85,7 @@ def build_trace(rng: np.random.Generator, N: int, P: int, budget: int,
     turns = []
     t = P
     while t < N:
-        L = _round_up16(rng.integers(lo, hi + 1)) if lo != hi else lo
+        L = _round_up(rng.integers(lo, hi + 1), granule) if lo != hi else lo
         end = min(t + L, N)
         turns.append((t, end))
         t = end
@@ -105,7 +109,8 @@ def build_trace(rng: np.random.Generator, N: int, P: int, budget: int,
         evicted[t_ev] = out
     return Trace(N=N, P=P, budget=budget, strategy=strategy, turns=turns,
                  events=events, evicted=evicted, e=e.astype(np.int32),
-                 live_units=list(units), overlap=overlap, summary=summary)
+                 live_units=list(units), overlap=overlap, summary=summary,
+                 granule=granule)
 
 
 def evict_units(units, t_ev, strategy, budget, P, overlap=0, summary=0):
@@ -146,9 +151,9 @@ def check_trace(tr: Trace) -> None:
     assert np.all(e > j), "e_j > j violated"
     ev = set(tr.events)
     assert all(int(x) in ev or int(x) == KS_NEVER for x in np.unique(e))
-    assert all(t % BLOCK == 0 for t in tr.events), "events must be 16-aligned"
-    assert all(x % BLOCK == 0 and (y % BLOCK == 0 or y == tr.N)
-               for (x, y) in tr.turns)
+    g = tr.granule
+    assert all(t % g == 0 for t in tr.events), "events must be granule-aligned"
+    assert all(x % g == 0 and (y % g == 0 or y == tr.N) for (x, y) in tr.turns)
     # live size at every query index is within budget:
     # |live(i)| = (i+1) - #{j <= i : e_j <= i}
     ev_hist = np.zeros(N + 1, dtype=np.int64)
@@ -230,9 +235,9 @@ class DecodeBatch:
     """Paged caches of several sequences before a run of compaction rounds.
 
     ``table0``      int32 [B, MB] physical block ids before any round (-1 pad);
-                    logical block x of sequence b holds tokens [16x, 16x+16),
-                    and the last listed block is a fresh block that receives the
-                    decoded token.
+                    logical block x of sequence b holds tokens
+                    [block*x, block*x + block), and the last listed block is a
+                    fresh block that receives the decoded token.
     ``nblk0``       int32 [B] listed blocks before any round.
     ``keeps``       uint8 [R, B, MB] keep flags for round r, relative to the
                     table as it stands before round r (zeros past the end).
@@ -242,6 +247,8 @@ class DecodeBatch:
     ``live_len``    int32 [B] live tokens before the decoded token (L_b).
     ``pos``         int32 [B] logical position of the decoded token (T_b).
     ``num_pool_blocks`` physical blocks in the pool.
+    ``block``       tokens per block (16, or 1 for single-token blocks, where
+                    the table lists token slots).
     """
     table0: np.ndarray
     nblk0: np.ndarray
@@ -251,30 +258,34 @@ class DecodeBatch:
     live_len: np.ndarray
     pos: np.ndarray
     num_pool_blocks: int
+    block: int = BLOCK
 
 
 def build_decode_batch(rng: np.random.Generator, n_seqs: int,
                        live_range=(4096, 16384), max_pos: int = 65536,
-                       events_range=(1, 6)) -> DecodeBatch:
+                       events_range=(1, 6), block: int = BLOCK) -> DecodeBatch:
     """Paged caches compacted by 1-6 events, then one decode step.
 
-    Per sequence: live length ``L`` uniform on the 16-aligned values of
+    Per sequence: live length ``L`` uniform on the ``block``-aligned values of
     ``live_range``; event count ``K`` uniform on ``events_range``; the
-    pre-compaction length ``T`` uniform 16-aligned on ``[L + 16K, max_pos]``.
-    The ``(T-L)/16`` evicted blocks form ``K`` runs of whole blocks that never
-    touch block 0 (the prompt) or the last block; run ``r`` is removed by event
-    ``r``.  Physical ids are a seeded permutation of the pool.  The decoded
-    token sits at logical position ``T`` in a fresh block appended to the
-    table, so ``seq_len = L + 1``.
+    pre-compaction length ``T`` uniform ``block``-aligned on
+    ``[L + block*K, max_pos]``.  The ``(T-L)/block`` evicted blocks form ``K``
+    runs of whole blocks that never touch block 0 (the prompt) or the last
+    block; run ``r`` is removed by event ``r``.  Physical ids are a seeded
+    permutation of the pool.  The decoded token sits at logical position
+    ``T`` in a fresh block appended to the table, so ``seq_len = L + 1``.
+    With ``block`` 1 every quantity is token-granular: turns and evicted runs
+    end anywhere and the table lists one pool slot per token.
     """
     lo, hi = live_range
+    bs = int(block)
     Ls, Ts, Ks, runs_all, evs_all = [], [], [], [], []
     for _ in range(n_seqs):
-        L = 16 * int(rng.integers(lo // 16, hi // 16 + 1))
+        L = bs * int(rng.integers(lo // bs, hi // bs + 1))
         K = int(rng.integers(events_range[0], events_range[1] + 1))
-        T = 16 * int(rng.integers((L + 16 * K) // 16, max_pos // 16 + 1))
-        nb_ev = (T - L) // 16
-        nb_keep = L // 16
+        T = bs * int(rng.integers((L + bs * K) // bs, max_pos // bs + 1))
+        nb_ev = (T - L) // bs
+        nb_keep = L // bs
         # sizes of the K evicted runs (each >= 1 block)
         cuts = np.sort(rng.choice(np.arange(1, nb_ev), K - 1, replace=False)) \
             if K > 1 else np.array([], dtype=np.int64)
@@ -287,13 +298,13 @@ def build_decode_batch(rng: np.random.Generator, n_seqs: int,
             x += int(gaps[r])
             runs.append((x, x + int(sizes[r])))
             x += int(sizes[r])
-        assert x + int(gaps[K]) == T // 16
+        assert x + int(gaps[K]) == T // bs
         # event r fires at the end of the kept gap that follows run r
-        evs = [16 * runs[r + 1][0] if r + 1 < K else T for r in range(K)]
+        evs = [bs * runs[r + 1][0] if r + 1 < K else T for r in range(K)]
         Ls.append(L); Ts.append(T); Ks.append(K)
         runs_all.append(runs); evs_all.append(evs)
 
-    nblk0 = np.array([T // 16 + 1 for T in Ts], dtype=np.int32)
+    nblk0 = np.array([T // bs + 1 for T in Ts], dtype=np.int32)
     MB = int(nblk0.max())
     NB = int(nblk0.sum())
     perm = rng.permutation(NB).astype(np.int32)
@@ -307,20 +318,20 @@ def build_decode_batch(rng: np.random.Generator, n_seqs: int,
     R = max(Ks)
     keeps = np.zeros((R, n_seqs, MB), dtype=np.uint8)
     for b in range(n_seqs):
-        logical = list(range(int(nblk0[b])))   # logical ids currently listed
+        logical = np.arange(int(nblk0[b]))          # logical ids currently listed
         for r in range(R):
             if r < Ks[b]:
                 x0, x1 = runs_all[b][r]
-                flags = [0 if x0 <= x < x1 else 1 for x in logical]
+                flags = (logical < x0) | (logical >= x1)
             else:
-                flags = [1] * len(logical)
+                flags = np.ones(len(logical), dtype=bool)
             keeps[r, b, :len(logical)] = flags
-            logical = [x for x, f in zip(logical, flags) if f]
+            logical = logical[flags]
     return DecodeBatch(table0=table0, nblk0=nblk0, keeps=keeps,
                        runs=runs_all, event_pos=evs_all,
                        live_len=np.array(Ls, dtype=np.int32),
                        pos=np.array(Ts, dtype=np.int32),
-                       num_pool_blocks=NB)
+                       num_pool_blocks=NB, block=bs)
 
 
 def normal_tensor(shape, seed: int, scale: float = 1.0, dtype=None,
