@@ -14,7 +14,9 @@ TFLOP/s of useful work (4*D flops forward and 10*D backward per live
 HIP events on the stream the kernels run on.  The decode side's HBM GB/s is
 reported beside it.  `single_token_blocks` times the same decode step with
 one pool slot per token (token tables, token-run compaction), and
-`reprefill_counterfactual` times, outside the step, the
+`toy_stack` reports the trainer/generator mismatch KL of a random-weight
+3-layer model built on the path, and `reprefill_counterfactual` times,
+outside the step, the
 attention that re-prefill compaction would run on the same rollouts.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same workload
 on the host cores.
@@ -376,6 +378,7 @@ def main():
                    for kk, vv in parts.items()},
     }
     result["single_token_blocks"] = token_granular_decode(ks, torch, stream, c4)
+    result["toy_stack"] = toy_stack_mismatch(torch)
     result["reprefill_counterfactual"] = reprefill_counterfactual(
         ks, torch, traces, q, k, v, do, stream, ms, pairs, c3)
     if not args.no_cpu_baseline:
@@ -458,6 +461,40 @@ def token_granular_decode(ks, torch, stream, cfg, reps=5):
         "decode_gbs": round(dec_bytes / (t_d * 1e-3) / 1e9, 1),
         "decode_plus_compact_frac": round((dec_bytes + comp_bytes) / ((t_c + t_d) * 1e-3)
                                           / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
+def toy_stack_mismatch(torch):
+    """A 3-layer random-weight decoder over the path: the masked training pass
+    and token-by-token generation over compacted paged caches on one 1024-token
+    trace (2+ events); the KL divergence of their next-token distributions is
+    the trainer/generator mismatch the pages quote (about 0.001 for theirs)."""
+    from kv_cache_compaction_amd.toy_stack import ToyStack
+    from workloads import ToyShape, build_trace, toy_tokens, toy_weights
+
+    shape = ToyShape()
+    tr = build_trace(np.random.default_rng(21), 1024, 64, 512, "recent", turn_len=(48, 160))
+    w = toy_weights(shape, 21)
+    stack = ToyStack(w, shape.Hq, shape.Hkv, shape.D)
+    tok = torch.from_numpy(toy_tokens(shape, tr.N, 21)).cuda()
+    e = torch.from_numpy(tr.e.astype(np.int32)).cuda()
+    stack.train_logits(tok, e)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    lt = stack.train_logits(tok, e)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ld = stack.decode_logits(tok, tr.evicted)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    lp, lq = torch.log_softmax(lt.double(), -1), torch.log_softmax(ld.double(), -1)
+    kl = (lp.exp() * (lp - lq)).sum(-1)
+    return {
+        "model": f"{shape.layers} layers, d_model {shape.d_model}, {shape.Hq} q / {shape.Hkv} kv "
+                 f"heads, D {shape.D}, random weights",
+        "tokens": int(tr.N), "events": len(tr.events),
+        "mismatch_kl_mean": float(kl.mean()), "mismatch_kl_max": float(kl.max()),
+        "train_pass_ms": round((t1 - t0) * 1e3, 2), "generation_ms": round((t2 - t1) * 1e3, 1),
     }
 
 

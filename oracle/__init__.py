@@ -10,3 +10,4 @@ from .ks_oracle import (  # noqa: F401
     attn_bwd_rows, attn_bwd_keys, compact_block_table, paged_decode,
     live_keys,
 )
+from . import toy_stack  # noqa: F401

@@ -2,9 +2,10 @@
 
 This package builds inputs only: turn boundaries, compaction-event records
 (the per-token eviction index e_j), paged block tables with per-round keep
-flags, the segment traces of the re-prefill counterfactual, and random tensors.  It holds none of the method's arithmetic (no RoPE,
-no attention, no table compaction); the oracle and the HIP library each
-implement those on their own.
+flags, the segment traces of the re-prefill counterfactual, random tensors
+and the random weights of a toy decoder stack.  It holds none of the
+method's arithmetic (no RoPE, no attention, no table compaction); the oracle
+and the HIP library each implement those on their own.
 """
 from .traces import (  # noqa: F401
     KS_NEVER, BLOCK, Trace, build_trace, check_trace, DecodeBatch, evict_units,
@@ -12,3 +13,4 @@ from .traces import (  # noqa: F401
     trace_blocks_keep,
 )
 from .configs import CONFIGS, Config, config_trace_batch, stacked_e  # noqa: F401
+from .toy import ToyShape, toy_tokens, toy_weights  # noqa: F401
