@@ -191,3 +191,29 @@ def test_bf16_end_to_end_rope_cfg2_shape():
     ro, rl = O.attn_fwd(O.rope(f64(q), pos), O.rope(f64(k), pos), f64(v), e)
     gate(o, ro, "bf16", "O")
     gate(lse, rl, "bf16", "LSE")
+
+
+def test_bf16_raw_projection_gradients_cfg2_shape():
+    """Gradients with respect to the raw q, k of the 4k workload: RoPE, masked
+    forward and backward on the GPU, then the inverse rotation of dQ, dK
+    (ks_rope_logical with inverse), against the oracle's gradients through
+    its own RoPE."""
+    cfg = CONFIGS[2]
+    traces, seeds = config_trace_batch(cfg)
+    e = stacked_e(traces)
+    B, N = cfg.batch, cfg.N
+    q, k, v, do = _inputs(B, N, cfg.Hq, cfg.Hkv, cfg.D, seeds["q"] + 11, torch.bfloat16)
+    pos = np.tile(np.arange(N, dtype=np.int32), (B, 1))
+    pg = torch.from_numpy(pos).to(DEV)
+    qg, kg, vg, dog = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    ks.ks_rope_logical(qg, kg, pg)
+    o, lse = ks.ks_evict_attn_fwd(qg, kg, vg, _e_gpu(e))
+    dq, dk, dv = ks.ks_evict_attn_bwd(qg, kg, vg, _e_gpu(e), o, lse, dog)
+    ks.ks_rope_logical(dq, dk, pg, inverse=True)
+    torch.cuda.synchronize()
+    qr, kr = O.rope(f64(q), pos), O.rope(f64(k), pos)
+    rdq, rdk, rdv = O.attn_bwd(qr, kr, f64(v), e, f64(do))
+    gate(dq, O.rope(rdq, pos, inverse=True), "bf16grad", "dQ raw")
+    gate(dk, O.rope(rdk, pos, inverse=True), "bf16grad", "dK raw")
+    gate(dv, rdv, "bf16grad", "dV")
+

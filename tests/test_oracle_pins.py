@@ -275,6 +275,40 @@ def test_bwd_matches_torch_autograd_sdpa():
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-11)
 
 
+def test_raw_projection_gradients_are_inverse_rotations():
+    """Gradients with respect to the raw (unrotated) q and k are the inverse
+    rotation of the gradients with respect to the rotated ones: checked by
+    torch autograd through a complex-number RoPE and masked SDPA in fp64."""
+    B, N, Hq, Hkv, D = 1, 80, 4, 2, 16
+    rng = np.random.default_rng(95)
+    e = random_e(rng, N, p_never=0.4)[None]
+    qr, kr, v = rnd((B, N, Hq, D), 96), rnd((B, N, Hkv, D), 97), rnd((B, N, Hkv, D), 98)
+    do = rnd((B, N, Hq, D), 99)
+    pos = (np.arange(N) + 1000)[None]
+    dq, dk, _ = O.attn_bwd(O.rope(qr, pos), O.rope(kr, pos), v, e, do)
+    gq, gk = O.rope(dq, pos, inverse=True), O.rope(dk, pos, inverse=True)
+    tq = torch.tensor(qr, requires_grad=True)
+    tk = torch.tensor(kr, requires_grad=True)
+    inv = 10000.0 ** (-2.0 * torch.arange(D // 2, dtype=torch.float64) / D)
+    rot = torch.polar(torch.ones(N, D // 2, dtype=torch.float64),
+                      torch.from_numpy(pos[0]).double()[:, None] * inv[None])
+
+    def rope(t):
+        c = torch.complex(t[..., :D // 2], t[..., D // 2:]) * rot[None, :, None]
+        return torch.cat([c.real, c.imag], -1)
+    i = torch.arange(N)[:, None]
+    j = torch.arange(N)[None, :]
+    mask = (j <= i) & (i < torch.from_numpy(e[0])[None, :])
+    G = Hq // Hkv
+    kk = rope(tk).repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    vv = torch.tensor(v).repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        rope(tq).permute(0, 2, 1, 3), kk, vv, attn_mask=mask)
+    out.backward(torch.from_numpy(do).permute(0, 2, 1, 3))
+    np.testing.assert_allclose(gq, tq.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(gk, tk.grad.numpy(), atol=1e-11)
+
+
 def test_bwd_invariants_and_sampled_variants():
     B, N, Hq, Hkv, D = 2, 120, 4, 2, 8
     rng = np.random.default_rng(100)
