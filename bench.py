@@ -120,7 +120,7 @@ def stored_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
     None when there is none or it was taken on other kernel sources."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        "hbm_traffic_cfg3_cfg4.json")
+                        "hbm_traffic_attn32k_decode64.json")
     try:
         with open(path) as fh:
             rec = json.load(fh)
@@ -159,9 +159,9 @@ class Timer:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by (trace, kv group) and by sequence without exchange, see "
-              "DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the path "
+              "would shard by (trace, kv group) for training and by sequence for decode, "
+              "with no exchange inside a step", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libks.so")
 SOURCES = ["ks_api.cpp", "compact.hip", "rope.hip", "decode.hip", "attn_fwd.hip",
            "attn_bwd.hip"]
 ARCH = "gfx950"
-# packed fp32 VALU ops are disabled on purpose (build flags)
+# packed fp32 VALU ops (v_pk_*_f32) are switched off: every kernel is built with
+# scalar fp32 VALU code only
 HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]

@@ -42,7 +42,7 @@ def _inputs(B, N, Hq, Hkv, D, seed, dtype, scale=0.5):
 
 
 # ---------------------------------------------------------------------------
-def test_cfg1_f32_rope_then_forward():
+def test_tiny512_f32_rope_then_forward():
     cfg = CONFIGS[1]
     (tr,), seeds = config_trace_batch(cfg)
     B, N, D = 1, cfg.N, cfg.D
@@ -76,7 +76,7 @@ def test_f32_forward_random_masks(N, G, seed):
 
 # ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
-def cfg2():
+def train4k():
     cfg = CONFIGS[2]
     traces, seeds = config_trace_batch(cfg)
     e = stacked_e(traces)
@@ -93,22 +93,22 @@ def cfg2():
                 ref=(ro, rl, rdq, rdk, rdv))
 
 
-def test_cfg2_forward(cfg2):
-    o, lse = cfg2["got"][:2]
-    ro, rl = cfg2["ref"][:2]
+def test_train4k_forward(train4k):
+    o, lse = train4k["got"][:2]
+    ro, rl = train4k["ref"][:2]
     gate(o, ro, "bf16", "O")
     gate(lse, rl, "bf16", "LSE")
 
 
-def test_cfg2_backward(cfg2):
-    for name, got, ref in zip(("dQ", "dK", "dV"), cfg2["got"][2:], cfg2["ref"][2:]):
+def test_train4k_backward(train4k):
+    for name, got, ref in zip(("dQ", "dK", "dV"), train4k["got"][2:], train4k["ref"][2:]):
         gate(got, ref, "bf16grad", name)
 
 
-def test_cfg2_negative_controls(cfg2):
+def test_train4k_negative_controls(train4k):
     """The gate must reject outputs compared against a wrong mask."""
-    o = cfg2["got"][0]
-    q, k, v, e = f64(cfg2["q"]), f64(cfg2["k"]), f64(cfg2["v"]), cfg2["e"]
+    o = train4k["got"][0]
+    q, k, v, e = f64(train4k["q"]), f64(train4k["k"]), f64(train4k["v"]), train4k["e"]
     N = e.shape[1]
     never = np.full_like(e, KS_NEVER)
     wrong_causal, _ = O.attn_fwd(q, k, v, never)
@@ -175,7 +175,7 @@ def test_bf16_diagonal_only_and_causal():
     gate(o2, ref, "bf16", "causal O")
 
 
-def test_bf16_end_to_end_rope_cfg2_shape():
+def test_bf16_end_to_end_rope_train4k():
     """RoPE at logical positions then the masked forward, against the oracle
     doing both in fp64 from the same raw projections."""
     cfg = CONFIGS[2]
@@ -193,7 +193,7 @@ def test_bf16_end_to_end_rope_cfg2_shape():
     gate(lse, rl, "bf16", "LSE")
 
 
-def test_bf16_raw_projection_gradients_cfg2_shape():
+def test_bf16_raw_projection_gradients_train4k():
     """Gradients with respect to the raw q, k of the 4k workload: RoPE, masked
     forward and backward on the GPU, then the inverse rotation of dQ, dK
     (ks_rope_logical with inverse), against the oracle's gradients through

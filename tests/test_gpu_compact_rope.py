@@ -24,7 +24,7 @@ def _gpu(a, dtype=None):
     return t if dtype is None else t.to(dtype)
 
 
-def test_compact_cfg1_table():
+def test_compact_tiny512_table():
     (tr,), _ = config_trace_batch(CONFIGS[1])
     perm = np.random.default_rng(7).permutation(32).astype(np.int32)[None]
     keep = trace_blocks_keep(tr)[None]
@@ -36,7 +36,7 @@ def test_compact_cfg1_table():
     np.testing.assert_array_equal(out.cpu().numpy(), ref)
 
 
-def test_compact_cfg4_rounds_pingpong():
+def test_compact_decode64_rounds_pingpong():
     db = build_decode_batch(np.random.default_rng(1004), 64)
     B, MB = db.table0.shape
     ta, tb = _gpu(db.table0), torch.empty((B, MB), dtype=torch.int32, device=DEV)
@@ -74,7 +74,7 @@ def _oracle_rounds(table, nblk, keeps, pos=None):
     return t, n, p
 
 
-def test_compact_rounds_cfg4_one_launch():
+def test_compact_rounds_decode64_one_launch():
     """All events of the decode workload in one launch equal the event-by-event oracle."""
     db = build_decode_batch(np.random.default_rng(1004), 64)
     B, MB = db.table0.shape
@@ -145,7 +145,7 @@ def test_compact_rejects_aliasing_on_device():
         ks.ks_compact_block_table(t, n, k, t, n)
 
 
-def test_rope_f32_cfg1_positions():
+def test_rope_f32_tiny512_positions():
     B, N, Hq, Hkv, D = 1, 512, 1, 1, 64
     q = normal_tensor((B, N, Hq, D), 11)
     k = normal_tensor((B, N, Hkv, D), 12)

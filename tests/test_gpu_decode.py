@@ -79,7 +79,7 @@ def run_decode_case(db, Hq, Hkv, D=128, seed=0, poison=True, base=10000.0):
     return out, lse, ro, rl
 
 
-def test_cfg4_full_compaction_then_decode():
+def test_decode64_full_compaction_then_decode():
     cfg = CONFIGS[4]
     db = build_decode_batch(np.random.default_rng(1000 + 4), cfg.batch)
     out, lse, ro, rl = run_decode_case(db, cfg.Hq, cfg.Hkv, seed=4000)

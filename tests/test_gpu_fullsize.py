@@ -82,7 +82,7 @@ def run_training_config(cfg, b, hkv, key_blocks):
         gate(dv[b, keys, hkv], rdv, "bf16grad", f"dV keys {keys[0]}..")
 
 
-def test_cfg3_summary_32k_sampled():
+def test_summary_32k_sampled():
     def key_blocks(tr):
         t1 = tr.events[0]
         return [np.arange(tr.N - 64, tr.N),                      # queries [j, N)

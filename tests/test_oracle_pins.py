@@ -374,8 +374,8 @@ def test_compaction_rounds_equal_union_and_conserve_tokens():
         assert all(a < c for a, c in zip(logical, logical[1:]))
 
 
-def test_cfg1_worked_example():
-    with open(os.path.join(GOLDEN, "cfg1_trace.json")) as f:
+def test_tiny512_worked_example():
+    with open(os.path.join(GOLDEN, "tiny512_trace.json")) as f:
         g = json.load(f)
     (tr,), _ = config_trace_batch(CONFIGS[1])
     assert tr.events == g["events"]
