@@ -102,17 +102,26 @@ def executed_flops(e: np.ndarray, Hq: int, Hkv: int, D: int, kt: int = 64):
     return fwd, dq, dkdv
 
 
-def kernel_sources_hash() -> str:
-    """sha256 over the HIP sources of libks (a stored counter summary applies
-    only to the kernels it was taken on)."""
+# HIP sources each entry point's kernels are built from (a stored counter
+# summary applies only to the kernels it was taken on)
+ENTRY_SOURCES = {
+    "ks_evict_attn_fwd": ("ks_common.h", "attn_common.h", "attn_fwd.hip"),
+    "ks_evict_attn_bwd": ("ks_common.h", "attn_common.h", "attn_fwd.hip", "attn_bwd.hip"),
+    "ks_paged_decode": ("ks_common.h", "decode.hip"),
+    "ks_paged_decode_bs1": ("ks_common.h", "decode.hip"),
+    "ks_compact_block_table_rounds": ("ks_common.h", "compact.hip"),
+}
+
+
+def kernel_sources_hash(entry: str) -> str:
+    """sha256 over the HIP sources of one entry point's kernels."""
     import hashlib
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kv_cache_compaction_amd",
                         "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(root)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(root, name), "rb") as fh:
-                h.update(name.encode() + b"\0" + fh.read())
+    for name in sorted(ENTRY_SOURCES[entry]):
+        with open(os.path.join(root, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
@@ -126,10 +135,12 @@ def stored_traffic(kernel: str):
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("sources_sha256") != kernel_sources_hash():
-        return None
     ent = rec.get("entry_points", {}).get(kernel)
-    return None if ent is None else ent.get("hbm_bytes_per_launch")
+    if ent is None or kernel not in ENTRY_SOURCES:
+        return None
+    if ent.get("sources_sha256") != kernel_sources_hash(kernel):
+        return None
+    return ent.get("hbm_bytes_per_launch")
 
 
 class Timer:

@@ -290,6 +290,30 @@ ks_status ks_append_kv_bs1(const void* k_new, const void* v_new,
                            int num_pool_tokens, int dtype, float base,
                            void* stream);
 
+/*
+ * Input checks (a debugging aid; nothing on the hot path depends on them).
+ *
+ * The kernels stay inside their buffers when the preconditions below are
+ * broken: a token with e_j <= j is seen by no query, and a table entry
+ * outside the pool makes that sequence's decode output NaN.  These calls
+ * count the violations instead, one int32 per sequence written to `bad`
+ * (device memory, [B]); a count of 0 means the input meets the
+ * preconditions.  Asynchronous on `stream` like every other call.
+ *
+ * ks_check_eviction_record  bad[b] = #{ j < N : e[b][j] <= j } for the
+ *     eviction record e int32 [B, N] of ks_evict_attn_fwd / _bwd.
+ * ks_check_block_table  bad[b] = #{ x < ceil(L_b / block_size) :
+ *     table[b][x] outside [0, num_pool_blocks) } + (1 if L_b < 0 or
+ *     L_b > block_size * max_blocks), with L_b = seq_lens[b] (clamped to
+ *     the row for the count); table int32 [B, max_blocks], block_size 16
+ *     (ks_paged_decode) or 1 (ks_paged_decode_bs1).
+ */
+ks_status ks_check_eviction_record(const int32_t* e, int B, int N, int32_t* bad,
+                                   void* stream);
+ks_status ks_check_block_table(const int32_t* table, const int32_t* seq_lens,
+                               int B, int max_blocks, int num_pool_blocks,
+                               int block_size, int32_t* bad, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,8 @@ _SIGS = {
     "ks_paged_decode_bs1_workspace": ([_i, _i, _i, _i], _sz),
     "ks_paged_decode_bs1": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
     "ks_append_kv_bs1": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _f, _vp], _i),
+    "ks_check_eviction_record": ([_vp, _i, _i, _vp, _vp], _i),
+    "ks_check_block_table": ([_vp, _vp, _i, _i, _i, _i, _vp, _vp], _i),
 }
 
 _lib = None
@@ -362,3 +364,32 @@ def ks_append_kv_bs1(k_new, v_new, pos, token_table, seq_lens, k_pool, v_pool, b
                               token_table.shape[1], NT, _dtype_code(k_new), float(base),
                               _stream(stream))
     _check("ks_append_kv_bs1", st)
+
+
+def ks_check_eviction_record(e, bad=None, stream=None):
+    """Per trace, the number of tokens j with e[b, j] <= j (int32 [B] on the device)."""
+    lib = load_library()
+    _cuda_contig("e", e, torch.int32)
+    _need(e.dim() == 2, "e must be [B, N]")
+    B, N = e.shape
+    bad = torch.empty(B, dtype=torch.int32, device=e.device) if bad is None else bad
+    _check("ks_check_eviction_record",
+           lib.ks_check_eviction_record(_ptr(e), B, N, _ptr(bad), _stream(stream)))
+    return bad
+
+
+def ks_check_block_table(table, seq_lens, num_pool_blocks, block_size=KS_BLOCK, bad=None,
+                         stream=None):
+    """Per sequence, the number of table entries a decode would reach that are not
+    pool indices, plus one if seq_lens[b] is negative or past the row."""
+    lib = load_library()
+    _cuda_contig("table", table, torch.int32)
+    _cuda_contig("seq_lens", seq_lens, torch.int32)
+    B, MB = table.shape
+    _need(tuple(seq_lens.shape) == (B,), "seq_lens shape")
+    bad = torch.empty(B, dtype=torch.int32, device=table.device) if bad is None else bad
+    _check("ks_check_block_table",
+           lib.ks_check_block_table(_ptr(table), _ptr(seq_lens), B, MB, int(num_pool_blocks),
+                                    int(block_size), _ptr(bad), _stream(stream)))
+    return bad
+

@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libks.so")
 
 SOURCES = ["ks_api.cpp", "compact.hip", "rope.hip", "decode.hip", "attn_fwd.hip",
-           "attn_bwd.hip"]
+           "attn_bwd.hip", "check.hip"]
 ARCH = "gfx950"
 # packed fp32 VALU ops (v_pk_*_f32) are switched off: every kernel is built with
 # scalar fp32 VALU code only

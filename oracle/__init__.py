@@ -8,6 +8,6 @@ library and never imports it.
 from .ks_oracle import (  # noqa: F401
     KS_NEVER, BLOCK, rope, eviction_mask, attn_fwd, attn_fwd_rows, attn_bwd,
     attn_bwd_rows, attn_bwd_keys, compact_block_table, paged_decode,
-    live_keys,
+    live_keys, count_bad_e, count_bad_table,
 )
 from . import toy_stack  # noqa: F401

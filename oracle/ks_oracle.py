@@ -274,3 +274,31 @@ def paged_decode(q, k_pool, v_pool, table, seq_lens, scale=None):
                 out[b, h] = (w / z) @ vals
                 lse[b, h] = m + math.log(z)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Input checks (counts of precondition violations)
+# ---------------------------------------------------------------------------
+def count_bad_e(e):
+    """Per trace, the tokens whose eviction index does not exceed their own
+    index (e_j <= j): such a token would be evicted before it exists."""
+    e = np.asarray(e, dtype=np.int64)
+    return np.array([sum(1 for j in range(e.shape[1]) if e[b, j] <= j)
+                     for b in range(e.shape[0])], dtype=np.int32)
+
+
+def count_bad_table(table, seq_lens, num_pool_blocks, block_size):
+    """Per sequence, the entries among the first ceil(L/BS) of its table row
+    (L clamped to the row) that are not pool indices, plus one if L is
+    negative or longer than the row can hold."""
+    table = np.asarray(table)
+    B, MB = table.shape
+    out = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        L = int(seq_lens[b])
+        cap = block_size * MB
+        n = 0 if L <= 0 else (min(L, cap) + block_size - 1) // block_size
+        bad = sum(1 for x in range(n) if not (0 <= int(table[b, x]) < num_pool_blocks))
+        out[b] = bad + (1 if (L < 0 or L > cap) else 0)
+    return out
+

@@ -12,7 +12,7 @@ import torch
 import kv_cache_compaction_amd as ks
 import oracle as O
 from parity_util import announce, f64, gate
-from workloads import CONFIGS, build_decode_batch, build_trace, check_trace, normal_tensor
+from workloads import CONFIGS, KS_NEVER, build_decode_batch, build_trace, check_trace, normal_tensor
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -269,3 +269,31 @@ def test_masked_attention_on_token_granular_trace():
     gate(dq, rdq, "bf16grad", "dQ")
     gate(dk, rdk, "bf16grad", "dK")
     gate(dv, rdv, "bf16grad", "dV")
+
+
+# ---------------------------------------------------------------------------
+# input checks
+# ---------------------------------------------------------------------------
+def test_input_checks_count_violations():
+    rng = np.random.default_rng(900)
+    B, N = 5, 3001
+    e = np.full((B, N), KS_NEVER, np.int32)
+    e[:, :N - 1] = np.arange(1, N)[None] + rng.integers(0, 50, size=(B, N - 1))
+    for b in range(1, B):          # plant violations
+        idx = rng.choice(N, size=b * 7, replace=False)
+        e[b, idx] = idx - rng.integers(0, 3, size=idx.size)
+    got = ks.ks_check_eviction_record(_gpu(e))
+    for BS, NB, MB in ((16, 300, 190), (1, 5000, 3001)):
+        table = rng.integers(0, NB, size=(B, MB)).astype(np.int32)
+        table[1, 5] = NB
+        table[2, 0] = -1
+        table[3, MB - 1] = NB + 100
+        seq = rng.integers(1, BS * MB + 1, size=B).astype(np.int32)
+        seq[3] = BS * MB
+        seq[4] = BS * MB + 3          # longer than the row
+        bt = ks.ks_check_block_table(_gpu(table), _gpu(seq), NB, BS)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bt.cpu().numpy(), O.count_bad_table(table, seq, NB, BS))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), O.count_bad_e(e))
+    assert got[0].item() == 0

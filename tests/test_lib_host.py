@@ -137,3 +137,12 @@ def test_single_token_block_argument_checks(lib):
     st, _ = _status(lib, "ks_append_kv_bs1", *([FAKE] * 7), 0, 8, 128, 10, 100, 1, 10000.0,
                     None)
     assert st == 0
+
+
+def test_input_check_argument_checks(lib):
+    st, _ = _status(lib, "ks_check_block_table", FAKE, FAKE, 2, 10, 10, 8, FAKE, None)
+    assert st == 1  # block size 8
+    st, _ = _status(lib, "ks_check_eviction_record", None, 0, 10, None, None)
+    assert st == 0  # nothing to check
+    st, _ = _status(lib, "ks_check_eviction_record", FAKE, -1, 10, FAKE, None)
+    assert st == 1

@@ -545,3 +545,19 @@ def test_token_decode_batch_structure():
     for r in range(db.keeps.shape[0]):
         out, n = O.compact_block_table(out, n, db.keeps[r])
     np.testing.assert_array_equal(n, db.live_len + 1)
+
+
+# ---------------------------------------------------------------------------
+# Input checks
+# ---------------------------------------------------------------------------
+def test_input_check_counts_hand_examples():
+    # e_j <= j at j = 0 (e = 0), j = 3 (e = 3), j = 4 (e = -7); e_j = j + 1 is fine
+    e = np.array([[0, 5, 9, 3, -7, 6], [1, 2, 3, 4, 5, KS_NEVER]])
+    np.testing.assert_array_equal(O.count_bad_e(e), [3, 0])
+    # 16-token blocks, pool of 10: row 0 reaches 2 entries (L = 17), one bad;
+    # row 1 L = 0 reaches none; row 2 L = 65 > 16 * 4: the 4 entries, two bad,
+    # plus one for the length; row 3 negative length
+    t = np.array([[3, -1, 7, 7], [11, 12, 13, 14], [0, 10, 9, -2], [1, 1, 1, 1]])
+    np.testing.assert_array_equal(O.count_bad_table(t, [17, 0, 65, -3], 10, 16), [1, 0, 3, 1])
+    # single-token blocks: L = 3 reaches 3 entries
+    np.testing.assert_array_equal(O.count_bad_table(t[:1], [3], 10, 1), [1])
