@@ -388,6 +388,7 @@ def main():
         "stages": {kk: {x: (round(y, 4) if isinstance(y, float) else y) for x, y in vv.items()}
                    for kk, vv in parts.items()},
     }
+    result["hbm_reference"] = hbm_reference(torch, stream)
     result["single_token_blocks"] = token_granular_decode(ks, torch, stream, c4)
     result["toy_stack"] = toy_stack_mismatch(torch)
     result["reprefill_counterfactual"] = reprefill_counterfactual(
@@ -395,6 +396,28 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(traces, seeds, c3, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def hbm_reference(torch, stream, nbytes=2 << 30, reps=5):
+    """What plain library kernels reach on this GPU's HBM, as context for the
+    decode and compaction figures: a device-to-device copy (read + write) and
+    a full read (a sum over fp32) of 2 GiB."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, traffic in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                              ("read", lambda: src.sum(), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[f"{name}_gbs"] = round(traffic / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+    del src, dst
+    return out
 
 
 def token_granular_decode(ks, torch, stream, cfg, reps=5):
