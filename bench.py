@@ -5,8 +5,9 @@ One step = one pass of every hot-path stage over one batch of synthetic input:
   D = 128, bf16): RoPE at logical positions on Q and K, eviction-masked
   attention forward, then backward;
   inference side (64 paged caches, 32 q / 8 kv heads): 1-6 rounds of
-  block-table compaction, RoPE of the decode query at its logical position,
-  one paged GQA decode step.
+  block-table compaction, the append of the new token (its key rotated at
+  its logical position), one paged GQA decode step with the query rotated
+  in the kernel's prologue.
 
 Prints one JSON line.  `value` is the masked attention fwd+bwd throughput in
 TFLOP/s of useful work (4*D flops forward and 10*D backward per live
@@ -233,10 +234,10 @@ def main():
     ws_d = torch.empty(ks.ks_paged_decode_workspace(DB, H4q, D, MB), dtype=torch.uint8,
                        device=dev)
     L = db.live_len.astype(np.int64) + 1
-    # decode step bytes: K/V of every live token once, q (rotated in place:
-    # read + write), the appended token's k/v (read + write), output, lse,
+    # decode step bytes: K/V of every live token once, q (read once, rotated
+    # in the kernel), the appended token's k/v (read + write), output, lse,
     # table entries and lengths
-    dec_bytes = int((L * H4kv * D * 2 * 2).sum()) + 2 * DB * H4q * D * 2 + \
+    dec_bytes = int((L * H4kv * D * 2 * 2).sum()) + DB * H4q * D * 2 + \
         2 * 2 * DB * H4kv * D * 2 + DB * H4q * D * 2 + DB * H4q * 4 + \
         int(((L + 15) // 16).sum()) * 4 + DB * 4
     # compaction bytes: the table rows and every event's keep flags read once,
@@ -269,10 +270,11 @@ def main():
         src = tbufs[0]
         t1(ev, "compact")
         ev = t0()
-        ks.ks_rope_logical(q4, None, pos4, stream=stream)
+        # the new token's k rotated and written by the append, the query
+        # rotated inside the decode kernel
         ks.ks_append_kv(k4, v4, pos4f, src, seq_lens, kp, vp, stream=stream)
-        ks.ks_paged_decode(q4[:, 0], kp, vp, src, seq_lens, out=out4, lse=lse4, ws=ws_d,
-                           stream=stream)
+        ks.ks_paged_decode_rope(q4[:, 0], pos4f, kp, vp, src, seq_lens, out=out4, lse=lse4,
+                                ws=ws_d, stream=stream)
         t1(ev, "decode")
 
     # q4[:, 0] is a view of a contiguous [B, 1, Hq, D] tensor: contiguous as [B, Hq, D]
@@ -440,7 +442,6 @@ def token_granular_decode(ks, torch, stream, cfg, reps=5):
     k_new = normal_tensor((B, Hkv, D), 8004, 0.5, bf, dev)
     v_new = normal_tensor((B, Hkv, D), 8005, 0.5, bf, dev)
     pos = torch.from_numpy(db.pos.astype(np.int32)).to(dev)
-    pos2 = pos[:, None].contiguous()
     table0 = torch.from_numpy(db.table0).to(dev)
     n0 = torch.from_numpy(db.nblk0).to(dev)
     keeps = torch.from_numpy(np.ascontiguousarray(db.keeps)).to(dev)     # [R, B, MT]
@@ -459,10 +460,9 @@ def token_granular_decode(ks, torch, stream, cfg, reps=5):
         return tb
 
     def decode(tab):
-        ks.ks_rope_logical(q, None, pos2, stream=stream)
         ks.ks_append_kv_bs1(k_new, v_new, pos, tab, seq_lens, kp, vp, stream=stream)
-        ks.ks_paged_decode_bs1(q0, kp, vp, tab, seq_lens, out=out, lse=lse, ws=ws,
-                               stream=stream)
+        ks.ks_paged_decode_rope(q0, pos, kp, vp, tab, seq_lens, out=out, lse=lse, ws=ws,
+                                stream=stream)
     tab = compact()
     decode(tab)
     torch.cuda.synchronize()
@@ -479,7 +479,7 @@ def token_granular_decode(ks, torch, stream, cfg, reps=5):
         t_d += ev[1].elapsed_time(ev[2])
     t_c, t_d = t_c / reps, t_d / reps
     L = db.live_len.astype(np.int64) + 1
-    dec_bytes = int((L * Hkv * D * 2 * 2).sum()) + 2 * B * Hq * D * 2 + \
+    dec_bytes = int((L * Hkv * D * 2 * 2).sum()) + B * Hq * D * 2 + \
         2 * 2 * B * Hkv * D * 2 + B * Hq * D * 2 + B * Hq * 4 + int(L.sum()) * 4 + B * 4
     # the table rows and every event's keep flags read once, the rows and
     # lengths written once

@@ -277,6 +277,34 @@ ks_status ks_paged_decode_bs1(const void* q, const void* k_pool,
                               void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ks_paged_decode_rope -- paged decode with the query's RoPE fused into the
+ * kernel's prologue.
+ *
+ * New queries continue the original position count (explainer, RoPE
+ * paragraph); here the unrotated query is rotated at its logical position
+ * inside the decode kernel instead of by a separate ks_rope_logical call.
+ * The rotation is bit-identical to ks_rope_logical's, so the result equals
+ * ks_rope_logical (on a copy of q) followed by ks_paged_decode.
+ *
+ * q           [B, Hq, D] bf16, UNROTATED (not modified)
+ * pos         int32 [B] logical position of each sequence's query
+ * block_size  16: pools [num_pool, Hkv, 16, D], table of block ids,
+ *                 workspace ks_paged_decode_workspace(B, Hq, D, max_entries);
+ *             1:  pools [num_pool, Hkv, D], table of token slots,
+ *                 workspace ks_paged_decode_bs1_workspace(B, Hq, D, max_entries)
+ * base        RoPE base (> 1)
+ * other arguments, outputs and errors as for ks_paged_decode.
+ */
+ks_status ks_paged_decode_rope(const void* q, const int32_t* pos,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* table, const int32_t* seq_lens,
+                               void* out, float* lse, int B, int Hq, int Hkv,
+                               int D, int max_entries, int num_pool,
+                               int block_size, int dtype, float scale,
+                               float base, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
  * ks_append_kv_bs1 -- ks_append_kv with single-token blocks: the new token's
  * rotated key and its value go to pool slot token_table[b][seq_lens[b] - 1].
  *

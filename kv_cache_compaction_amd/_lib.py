@@ -50,6 +50,7 @@ _SIGS = {
     "ks_paged_decode_bs1_workspace": ([_i, _i, _i, _i], _sz),
     "ks_paged_decode_bs1": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
     "ks_append_kv_bs1": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _f, _vp], _i),
+    "ks_paged_decode_rope": ([_vp] * 8 + [_i] * 8 + [_f, _f, _vp, _sz, _vp], _i),
     "ks_check_eviction_record": ([_vp, _i, _i, _vp, _vp], _i),
     "ks_check_block_table": ([_vp, _vp, _i, _i, _i, _i, _vp, _vp], _i),
 }
@@ -392,4 +393,43 @@ def ks_check_block_table(table, seq_lens, num_pool_blocks, block_size=KS_BLOCK, 
            lib.ks_check_block_table(_ptr(table), _ptr(seq_lens), B, MB, int(num_pool_blocks),
                                     int(block_size), _ptr(bad), _stream(stream)))
     return bad
+
+
+def ks_paged_decode_rope(q, pos, k_pool, v_pool, table, seq_lens, base=10000.0, scale=None,
+                         out=None, lse=None, ws=None, stream=None):
+    """Paged decode of the UNROTATED query q [B, Hq, D], rotated inside the kernel
+    at pos [B].  Pools [NB, Hkv, 16, D] (16-token blocks) or [slots, Hkv, D]
+    (single-token blocks).  Returns (out, lse); q is not modified."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    if k_pool.dim() == 4:
+        NP, Hkv, BS, _ = k_pool.shape
+        _need(BS == KS_BLOCK, "pool block size must be 16")
+    else:
+        _need(k_pool.dim() == 3, "pool must be [NB, Hkv, 16, D] or [slots, Hkv, D]")
+        NP, Hkv, _ = k_pool.shape
+        BS = 1
+    _cuda_contig("q", q)
+    _cuda_contig("pos", pos, torch.int32)
+    _cuda_contig("k_pool", k_pool, q.dtype)
+    _cuda_contig("v_pool", v_pool, q.dtype)
+    _cuda_contig("table", table, torch.int32)
+    _cuda_contig("seq_lens", seq_lens, torch.int32)
+    _need(tuple(v_pool.shape) == tuple(k_pool.shape), "v_pool shape")
+    _need(table.shape[0] == B and tuple(seq_lens.shape) == (B,) and tuple(pos.shape) == (B,),
+          "table/seq_lens/pos shape")
+    ME = table.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    nbytes = (lib.ks_paged_decode_workspace(B, Hq, D, max(ME, 1)) if BS == KS_BLOCK
+              else lib.ks_paged_decode_bs1_workspace(B, Hq, D, max(ME, 1)))
+    ws = _workspace(nbytes, q.device, ws)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.ks_paged_decode_rope(_ptr(q), _ptr(pos), _ptr(k_pool), _ptr(v_pool), _ptr(table),
+                                  _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, ME, NP,
+                                  BS, _dtype_code(q), sc, float(base), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _check("ks_paged_decode_rope", st)
+    return out, lse
 

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const bf16_t* __restrict__ vpool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
     float* __restrict__ part_ml, int Hq, int Hkv, int MB, int NB, int nsplit_max,
-    float sl2) {
+    float sl2, const int32_t* __restrict__ qpos, double log2_base) {
   static_assert(BS == 16 || BS == 1, "block size");
   const int hw = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
@@ -197,6 +197,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 
   BlockRegs r0, r1;
   load(blk0, r0);
+  if (qpos) {
+    // q arrives unrotated: rotate it at its logical position.  Lane k forms
+    // (cos, sin) of pair k once; lane (t, g) holds d = 32 s + 8 g + i, so its
+    // pairs (d, d + 64) are fragments s and s + 2 of its own registers.
+    const float2 csl = rope_cos_sin(static_cast<double>(qpos[b]), lane, D, log2_base);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kk = 32 * s + 8 * g + i;
+        const float2 cs = make_float2(__shfl(csl.x, kk), __shfl(csl.y, kk));
+        float x = static_cast<float>(qa[s][i]), y = static_cast<float>(qa[s + 2][i]);
+        rope_rotate(x, y, cs);
+        qa[s][i] = static_cast<__bf16>(x);
+        qa[s + 2][i] = static_cast<__bf16>(y);
+      }
+  }
   int blk = blk0;
   for (; blk + 1 < blk1; blk += 2) {
     load(blk + 1, r1);
@@ -281,12 +298,8 @@ __global__ __launch_bounds__(256) void append_kernel(
   const int slot = L - 1;
   const int pid = table[static_cast<size_t>(b) * MB + slot / BS];
   if (static_cast<unsigned>(pid) >= static_cast<unsigned>(NB)) return;
-  for (int kk = threadIdx.x; kk < D / 2; kk += blockDim.x) {
-    const double inv_freq = exp2(-2.0 * kk / D * log2_base);
-    double sn, c;
-    sincos(static_cast<double>(pos[b]) * inv_freq, &sn, &c);
-    cs[kk] = make_float2(static_cast<float>(c), static_cast<float>(sn));
-  }
+  for (int kk = threadIdx.x; kk < D / 2; kk += blockDim.x)
+    cs[kk] = rope_cos_sin(static_cast<double>(pos[b]), kk, D, log2_base);
   __syncthreads();
   // thread = (head, 8-element chunk of the first half)
   for (int idx = threadIdx.x; idx < Hkv * (D / 16); idx += blockDim.x) {
@@ -298,11 +311,12 @@ __global__ __launch_bounds__(256) void append_kernel(
     u32x4 ra, rb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float2 c0 = cs[ch * 8 + 2 * i], c1 = cs[ch * 8 + 2 * i + 1];
-      const float x0 = lo_bf16(a[i]), x1 = hi_bf16(a[i]);
-      const float y0 = lo_bf16(bb[i]), y1 = hi_bf16(bb[i]);
-      ra[i] = pack_bf16x2(x0 * c0.x - y0 * c0.y, x1 * c1.x - y1 * c1.y);
-      rb[i] = pack_bf16x2(y0 * c0.x + x0 * c0.y, y1 * c1.x + x1 * c1.y);
+      float x0 = lo_bf16(a[i]), x1 = hi_bf16(a[i]);
+      float y0 = lo_bf16(bb[i]), y1 = hi_bf16(bb[i]);
+      rope_rotate(x0, y0, cs[ch * 8 + 2 * i]);
+      rope_rotate(x1, y1, cs[ch * 8 + 2 * i + 1]);
+      ra[i] = pack_bf16x2(x0, x1);
+      rb[i] = pack_bf16x2(y0, y1);
     }
     *reinterpret_cast<u32x4*>(kpool + dst) = ra;
     *reinterpret_cast<u32x4*>(kpool + dst + D / 2) = rb;
@@ -325,7 +339,8 @@ template <int BS>
 ks_status decode_impl(const char* name, const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* table, const int32_t* seq_lens, void* out, float* lse, int B,
                       int Hq, int Hkv, int Dh, int max_entries, int num_pool, int dtype,
-                      float scale, void* ws, size_t ws_bytes, void* stream) {
+                      float scale, void* ws, size_t ws_bytes, void* stream,
+                      const int32_t* qpos = nullptr, float base = 0.f) {
   KS_REQUIRE(B >= 0 && Hq > 0 && Hkv > 0 && max_entries >= 0 && num_pool >= 0,
              "%s: bad sizes", name);
   KS_REQUIRE(Hq % Hkv == 0, "%s: Hq %% Hkv != 0", name);
@@ -339,6 +354,7 @@ ks_status decode_impl(const char* name, const void* q, const void* k_pool, const
   KS_REQUIRE(q && k_pool && v_pool && table && seq_lens && out, "%s: null pointer", name);
   KS_REQUIRE(ks_aligned16(q) && ks_aligned16(k_pool) && ks_aligned16(v_pool) && ks_aligned16(out),
              "%s: tensors must be 16-byte aligned", name);
+  const double log2_base = qpos ? log2(static_cast<double>(base)) : 0.0;
   KS_REQUIRE(static_cast<int64_t>(max_entries) * BS < (int64_t{1} << 31),
              "%s: table row too long", name);
   // max_entries == 0: every length clamps to 0 and no table entry is read
@@ -362,13 +378,16 @@ ks_status decode_impl(const char* name, const void* q, const void* k_pool, const
   const bf16_t* vp = static_cast<const bf16_t*>(v_pool);
   if (hpw == 4)
     hipLaunchKernelGGL((decode_split_kernel<4, BS>), grid, dim3(64), 0, s, qq, kp, vp, table,
-                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2);
+                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2,
+                       qpos, log2_base);
   else if (hpw == 2)
     hipLaunchKernelGGL((decode_split_kernel<2, BS>), grid, dim3(64), 0, s, qq, kp, vp, table,
-                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2);
+                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2,
+                       qpos, log2_base);
   else
     hipLaunchKernelGGL((decode_split_kernel<1, BS>), grid, dim3(64), 0, s, qq, kp, vp, table,
-                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2);
+                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2,
+                       qpos, log2_base);
   ks_status st = ks_check_launch(name);
   if (st != KS_OK) return st;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(Hq, B), dim3(D), 0, s, part_o, part_ml, seq_lens,
@@ -430,6 +449,25 @@ extern "C" ks_status ks_paged_decode_bs1(const void* q, const void* k_pool, cons
   return decode_impl<1>("ks_paged_decode_bs1", q, k_pool, v_pool, token_table, seq_lens, out,
                         lse, B, Hq, Hkv, Dh, max_tokens, num_pool_tokens, dtype, scale, ws,
                         ws_bytes, stream);
+}
+
+extern "C" ks_status ks_paged_decode_rope(const void* q, const int32_t* pos, const void* k_pool,
+                                          const void* v_pool, const int32_t* table,
+                                          const int32_t* seq_lens, void* out, float* lse, int B,
+                                          int Hq, int Hkv, int Dh, int max_entries,
+                                          int num_pool, int block_size, int dtype, float scale,
+                                          float base, void* ws, size_t ws_bytes, void* stream) {
+  KS_REQUIRE(block_size == 16 || block_size == 1, "ks_paged_decode_rope: block_size %d",
+             block_size);
+  KS_REQUIRE(base > 1.0f, "ks_paged_decode_rope: base must be > 1");
+  if (B > 0) KS_REQUIRE(pos, "ks_paged_decode_rope: pos is NULL");
+  if (block_size == 16)
+    return decode_impl<16>("ks_paged_decode_rope", q, k_pool, v_pool, table, seq_lens, out, lse,
+                           B, Hq, Hkv, Dh, max_entries, num_pool, dtype, scale, ws, ws_bytes,
+                           stream, pos, base);
+  return decode_impl<1>("ks_paged_decode_rope", q, k_pool, v_pool, table, seq_lens, out, lse, B,
+                        Hq, Hkv, Dh, max_entries, num_pool, dtype, scale, ws, ws_bytes, stream,
+                        pos, base);
 }
 
 extern "C" ks_status ks_append_kv(const void* k_new, const void* v_new, const int32_t* pos,

@@ -54,6 +54,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// RoPE at logical position (rotate-half pairing of k and k + D/2): the angle
+// theta = pos * base^(-2k/D) is formed and reduced in fp64 (positions reach
+// the tens of thousands, where an fp32 angle is off by ~1e-3 rad), then the
+// pair rotates in fp32.  Every kernel that rotates uses these two helpers,
+// so a key or query rotated by any of them is bit-identical.
+__device__ __forceinline__ float2 rope_cos_sin(double pos, int k, int D, double log2_base,
+                                               bool inverse = false) {
+  const double inv_freq = exp2(-2.0 * k / D * log2_base);
+  double theta = pos * inv_freq;
+  if (inverse) theta = -theta;
+  double s, c;
+  sincos(theta, &s, &c);
+  return make_float2(static_cast<float>(c), static_cast<float>(s));
+}
+// (x, y) = (x[k], x[k + D/2]) -> (x cos - y sin, y cos + x sin)
+__device__ __forceinline__ void rope_rotate(float& x, float& y, float2 cs) {
+  const float xr = __builtin_fmaf(x, cs.x, -(y * cs.y));
+  const float yr = __builtin_fmaf(y, cs.x, x * cs.y);
+  x = xr;
+  y = yr;
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -8,8 +8,8 @@
 //
 // A workgroup handles kTok tokens.  The angles theta_k = pos * base^(-2k/D)
 // are formed in fp64 (positions reach 65,792, where an fp32 angle would be off
-// by ~4e-3 rad), reduced by the device library's fp64 sincos and kept in LDS
-// as fp32 pairs, shared by every head of the token.  Each thread then rotates
+// by ~4e-3 rad), reduced by the device library's fp64 sincos (rope_cos_sin)
+// and kept in LDS as fp32 pairs, shared by every head of the token.  Each thread then rotates
 // vector chunks of (x[k], x[k + D/2]): 8 bf16 or 4 fp32 per half.  The pass
 // streams Q and K once (read + write), so it is HBM bound.
 #include "ks_common.h"
@@ -36,22 +36,22 @@ struct Vec<bf16_t> {
 __device__ __forceinline__ void rot_chunk(f32x4& a, f32x4& b, const float2* cs) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float c = cs[i].x, s = cs[i].y;
-    const float x = a[i], y = b[i];
-    a[i] = x * c - y * s;
-    b[i] = y * c + x * s;
+    float x = a[i], y = b[i];
+    rope_rotate(x, y, cs[i]);
+    a[i] = x;
+    b[i] = y;
   }
 }
 
 __device__ __forceinline__ void rot_chunk(u32x4& a, u32x4& b, const float2* cs) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float c0 = cs[2 * i].x, s0 = cs[2 * i].y;
-    const float c1 = cs[2 * i + 1].x, s1 = cs[2 * i + 1].y;
-    const float x0 = lo_bf16(a[i]), x1 = hi_bf16(a[i]);
-    const float y0 = lo_bf16(b[i]), y1 = hi_bf16(b[i]);
-    a[i] = pack_bf16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
-    b[i] = pack_bf16x2(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+    float x0 = lo_bf16(a[i]), x1 = hi_bf16(a[i]);
+    float y0 = lo_bf16(b[i]), y1 = hi_bf16(b[i]);
+    rope_rotate(x0, y0, cs[2 * i]);
+    rope_rotate(x1, y1, cs[2 * i + 1]);
+    a[i] = pack_bf16x2(x0, x1);
+    b[i] = pack_bf16x2(y0, y1);
   }
 }
 
@@ -68,14 +68,8 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ q, T* __
   for (int idx = threadIdx.x; idx < kTok * half; idx += kThreads) {
     const int tt = idx / half, kk = idx - tt * half;
     const long long t = t0 + tt;
-    if (t < ntok) {
-      const double inv_freq = exp2(-2.0 * kk / D * log2_base);
-      double theta = static_cast<double>(pos[t]) * inv_freq;
-      if (inverse) theta = -theta;
-      double s, c;
-      sincos(theta, &s, &c);
-      cs[tt][kk] = make_float2(static_cast<float>(c), static_cast<float>(s));
-    }
+    if (t < ntok)
+      cs[tt][kk] = rope_cos_sin(static_cast<double>(pos[t]), kk, D, log2_base, inverse != 0);
   }
   __syncthreads();
   const int cpr = half / V;  // chunks per head

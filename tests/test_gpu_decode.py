@@ -165,3 +165,51 @@ def test_append_kv_rotates_and_places():
         assert torch.equal(vp[p, :, s % 16], v_new[b])
         touched[p, :, s % 16] = True
     assert torch.equal(kp[~touched], k0[~touched]) and torch.equal(vp[~touched], v0[~touched])
+
+
+@pytest.mark.parametrize("block", [16, 1])
+def test_fused_rope_decode_equals_rope_then_decode(block):
+    """ks_paged_decode_rope on the unrotated query equals ks_rope_logical then
+    the decode, bit for bit, on the 64-sequence batch (16-token and
+    single-token blocks); the query is left unrotated."""
+    db = build_decode_batch(np.random.default_rng(1000 + 4), 64, block=block)
+    B, MB = db.table0.shape
+    Hq, Hkv, D = 32, 8, 128
+    shape = (db.num_pool_blocks, Hkv, 16, D) if block == 16 else (db.num_pool_blocks, Hkv, D)
+    kp = normal_tensor(shape, 9001, 0.5, torch.bfloat16, DEV)
+    vp = normal_tensor(shape, 9002, 0.5, torch.bfloat16, DEV)
+    q = normal_tensor((B, Hq, D), 9003, 0.5, torch.bfloat16, DEV)
+    q0 = q.clone()
+    out_t, n_t, _ = ks.ks_compact_block_table_rounds(_gpu(db.table0), _gpu(db.nblk0),
+                                                     _gpu(db.keeps))
+    seq = _gpu((db.live_len + 1).astype(np.int32))
+    pos = _gpu(db.pos.astype(np.int32))
+    qr = q.clone()[:, None].contiguous()
+    ks.ks_rope_logical(qr, None, pos[:, None].contiguous())
+    if block == 16:
+        ref, ref_l = ks.ks_paged_decode(qr[:, 0].contiguous(), kp, vp, out_t, seq)
+    else:
+        ref, ref_l = ks.ks_paged_decode_bs1(qr[:, 0].contiguous(), kp, vp, out_t, seq)
+    got, got_l = ks.ks_paged_decode_rope(q, pos, kp, vp, out_t, seq)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q0)
+    assert torch.equal(got, ref) and torch.equal(got_l, ref_l)
+
+
+def test_fused_rope_decode_against_oracle():
+    db = build_decode_batch(np.random.default_rng(31), 5, live_range=(160, 1200), max_pos=60000)
+    B, MB = db.table0.shape
+    Hq, Hkv, D = 8, 2, 128
+    kp = normal_tensor((db.num_pool_blocks, Hkv, 16, D), 3101, 0.5, torch.bfloat16, DEV)
+    vp = normal_tensor((db.num_pool_blocks, Hkv, 16, D), 3102, 0.5, torch.bfloat16, DEV)
+    q = normal_tensor((B, Hq, D), 3103, 0.5, torch.bfloat16, DEV)
+    t, n, _ = ks.ks_compact_block_table_rounds(_gpu(db.table0), _gpu(db.nblk0), _gpu(db.keeps))
+    L = db.live_len + 1
+    out, lse = ks.ks_paged_decode_rope(q, _gpu(db.pos.astype(np.int32)), kp, vp, t,
+                                       _gpu(L.astype(np.int32)))
+    torch.cuda.synchronize()
+    qr = O.rope(f64(q)[:, None], db.pos[:, None])[:, 0]
+    ro, rl = O.paged_decode(qr, kp.float().cpu().numpy(), vp.float().cpu().numpy(),
+                            t.cpu().numpy(), L)
+    gate(out, ro, "bf16", "fused decode out")
+    gate(lse, rl, "bf16", "fused decode lse")

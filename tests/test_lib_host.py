@@ -146,3 +146,30 @@ def test_input_check_argument_checks(lib):
     assert st == 0  # nothing to check
     st, _ = _status(lib, "ks_check_eviction_record", FAKE, -1, 10, FAKE, None)
     assert st == 1
+
+
+def test_fused_rope_decode_argument_checks(lib):
+    st, msg = _status(lib, "ks_paged_decode_rope", *([FAKE] * 8), 2, 32, 8, 128, 10, 100, 8,
+                      1, 0.1, 10000.0, FAKE, 1 << 20, None)
+    assert st == 1 and "block_size" in msg
+    st, msg = _status(lib, "ks_paged_decode_rope", *([FAKE] * 8), 2, 32, 8, 128, 10, 100, 16,
+                      1, 0.1, 0.5, FAKE, 1 << 20, None)
+    assert st == 1 and "base" in msg
+    need = lib.ks_paged_decode_workspace(2, 32, 128, 10)
+    st, msg = _status(lib, "ks_paged_decode_rope", *([FAKE] * 8), 2, 32, 8, 128, 10, 100, 16,
+                      1, 0.1, 10000.0, FAKE, need - 1, None)
+    assert st == 4 and "workspace" in msg
+
+
+def test_binding_signatures_match_header():
+    """Every function the binding describes has the header's parameter count
+    (a wrong count would pass garbage through ctypes without an error)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", open(ks._lib.HEADER).read(), flags=re.S)
+    decls = dict(re.findall(r"\b(ks_[a-z0-9_]+)\s*\(([^;{]*)\)\s*;", text))
+    for name, (args, _) in _lib._SIGS.items():
+        assert name in decls, name
+        params = decls[name].strip()
+        n = 0 if params in ("", "void") else len(params.split(","))
+        assert n == len(args), (name, n, len(args))
+
