@@ -75,20 +75,29 @@ class ToyStack:
             x = self._mlp_out(L, x, o[0])
         return self._logits(x)
 
-    def decode_logits(self, tokens: torch.Tensor, evicted: dict) -> torch.Tensor:
+    def decode_logits(self, tokens: torch.Tensor, evicted: dict, block_size: int = BLOCK
+                      ) -> torch.Tensor:
         """fp32 logits [N, vocab], generating one token at a time.
 
         ``evicted`` maps an event index t to the token spans removed before
-        token t (whole 16-token blocks: the 16-padded turns of the vLLM
-        setup).  Every layer has its own pool; one block table serves all of
-        them.  At an event the table is spliced with ks_compact_block_table.
+        token t.  With ``block_size`` 16 (the vLLM setup) the spans must be
+        whole 16-token blocks, as padded turns make them; with 1 (SGLang's
+        single-token blocks) any span works.  Every layer has its own pool;
+        one table serves all of them and is spliced with
+        ks_compact_block_table at each event.  The new token's key is rotated
+        by the append, its query inside the decode kernel.
         """
+        if block_size not in (1, BLOCK):
+            raise ValueError(f"block_size {block_size} (1 or {BLOCK})")
+        bs = block_size
         N = tokens.shape[0]
         nl = len(self.layers)
-        MB = N // BLOCK + 2
+        MB = N // bs + 2
         bf = torch.bfloat16
-        kp = torch.zeros((nl, MB, self.Hkv, BLOCK, self.D), dtype=bf, device=self.dev)
+        shape = (nl, MB, self.Hkv, bs, self.D) if bs > 1 else (nl, MB, self.Hkv, self.D)
+        kp = torch.zeros(shape, dtype=bf, device=self.dev)
         vp = torch.zeros_like(kp)
+        append = K.ks_append_kv if bs > 1 else K.ks_append_kv_bs1
         table_h = []                      # block ids, in order
         first_tok = []                    # logical first token of each listed block
         nxt_block = 0
@@ -101,8 +110,8 @@ class ToyStack:
             if t in evicted:
                 gone = np.zeros(N, bool)
                 for (a, b) in evicted[t]:
-                    if a % BLOCK or b % BLOCK:
-                        raise ValueError("evicted spans must be whole 16-token blocks")
+                    if a % bs or b % bs:
+                        raise ValueError(f"evicted spans must be whole {bs}-token blocks")
                     gone[a:b] = True
                 keep = np.array([0 if gone[f] else 1 for f in first_tok], np.uint8)
                 kp_row = np.zeros((1, MB), np.uint8)
@@ -110,10 +119,10 @@ class ToyStack:
                 nblk.fill_(len(table_h))
                 table, nblk, _ = K.ks_compact_block_table(
                     table, nblk, torch.from_numpy(kp_row).to(self.dev))
-                live -= int(BLOCK * (len(keep) - keep.sum()))
+                live -= int(bs * (len(keep) - keep.sum()))
                 table_h = [b for b, k in zip(table_h, keep) if k]
                 first_tok = [f for f, k in zip(first_tok, keep) if k]
-            if live % BLOCK == 0:         # the new token opens a block
+            if live % bs == 0:            # the new token opens a block
                 table_h.append(nxt_block)
                 first_tok.append(t)
                 table[0, len(table_h) - 1] = nxt_block
@@ -124,11 +133,10 @@ class ToyStack:
             x = self.emb[tokens[t:t + 1]]
             for li, L in enumerate(self.layers):
                 q, k, v = self._qkv(L, x)
-                q = q[None].contiguous()                       # [1, 1, Hq, D]
-                K.ks_rope_logical(q, None, pos[None], base=self.base)
-                K.ks_append_kv(k.contiguous(), v.contiguous(), pos, table, seq, kp[li], vp[li],
-                               base=self.base)
-                o, _ = K.ks_paged_decode(q[:, 0].contiguous(), kp[li], vp[li], table, seq)
+                append(k.contiguous(), v.contiguous(), pos, table, seq, kp[li], vp[li],
+                       base=self.base)
+                o, _ = K.ks_paged_decode_rope(q.contiguous(), pos, kp[li], vp[li], table, seq,
+                                              base=self.base)
                 x = self._mlp_out(L, x, o)
             out[t] = self._logits(x)[0]
         return out

@@ -57,3 +57,30 @@ def test_training_pass_matches_generation(strategy, seed):
     lk = stack.decode_logits(tg, {}).cpu().numpy()
     t1 = tr.events[0]
     assert T.kl_rows(lt[t1:], lk[t1:]).mean() > 10 * KL_MEAN
+
+
+def test_single_token_blocks_generation_matches():
+    """The SGLang setup: turns of any length (no padding to 16), token-run
+    eviction, generation over single-token blocks; the training pass is the
+    same masked call."""
+    rng = np.random.default_rng(23)
+    tr = build_trace(rng, 1024, 61, 512, "recent", turn_len=(37, 151), granule=1)
+    check_trace(tr)
+    assert len(tr.events) >= 2 and any(t % 16 for t in tr.events)
+    w = toy_weights(SHAPE, 23)
+    tok = toy_tokens(SHAPE, tr.N, 23)
+    stack = ToyStack(w, SHAPE.Hq, SHAPE.Hkv, SHAPE.D)
+    tg = torch.from_numpy(tok).to(DEV)
+    lt = stack.train_logits(tg, torch.from_numpy(tr.e.astype(np.int32)).to(DEV))
+    ld = stack.decode_logits(tg, tr.evicted, block_size=1)
+    with pytest.raises(ValueError):
+        stack.decode_logits(tg[:4], {1: [(0, 1)]}, block_size=16)   # span not block-aligned
+    torch.cuda.synchronize()
+    ref = T.train_logits(w, tok, tr.e, SHAPE.Hq, SHAPE.Hkv, SHAPE.D)
+    lt, ld = lt.cpu().numpy(), ld.cpu().numpy()
+    for name, a, b in (("train vs oracle", ref, lt), ("decode vs oracle", ref, ld),
+                       ("train vs decode (mismatch)", lt, ld)):
+        kl = T.kl_rows(a, b)
+        announce(f"single-token {name}: KL mean {kl.mean():.3g} max {kl.max():.3g}")
+        assert kl.mean() <= KL_MEAN and kl.max() <= KL_MAX, (name, kl.mean(), kl.max())
+
