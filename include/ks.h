@@ -102,7 +102,10 @@ ks_status ks_rope_logical(void* q, void* k, const int32_t* pos, int B, int N,
  *
  * q    [B, N, Hq, D]   (rotated; dtype)
  * k, v [B, N, Hkv, D]  (k rotated; dtype)
- * e    int32 [B, N]    must satisfy e_j > j; any value >= N means "never"
+ * e    int32 [B, N]    must satisfy e_j > j; any value >= N means "never".
+ *                      (If it does not, token j is seen by no query; a row
+ *                      that sees no key gets O = 0 and LSE = -inf, and no
+ *                      gradient flows through it.)
  * o    [B, N, Hq, D]   output (dtype)
  * lse  float [B, Hq, N] output, natural log, may be NULL
  * dtype KS_BF16 (D = 128 or 64, fp32 accumulation) or KS_F32 (D <= 128,

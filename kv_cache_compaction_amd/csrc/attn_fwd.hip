@@ -160,7 +160,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
   }
   if (rv) {
     float* op = o + ((static_cast<size_t>(b) * N + i) * Hq + hq) * DH;
-    const float inv = 1.f / l;
+    const float inv = l > 0.f ? 1.f / l : 0.f;  // a row that sees no key: O = 0
 #pragma unroll
     for (int d = 0; d < DH; ++d) op[d] = acc[d] * inv;
     if (lse) lse[(static_cast<size_t>(b) * Hq + hq) * N + i] = (m + log2f(l)) * KS_LN2;
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lt = lrow[qb] + __shfl_xor(lrow[qb], 32);
-    const float inv = 1.f / lt;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a row that sees no key: O = 0
     const int i = wi0 + qb * 32 + lq;
     if (i < N) {
       bf16_t* op = o + (static_cast<size_t>(b) * N + i) * Hq * DH + static_cast<size_t>(hq) * DH;
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const float ltot = lrow + __shfl_xor(lrow, 32);
   if (qi < N) {
-    const float inv = 1.f / ltot;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // a row that sees no key: O = 0
     bf16_t* op = o + (static_cast<size_t>(b) * N + qi) * Hq * D + static_cast<size_t>(hq) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)

@@ -105,11 +105,15 @@ def attn_fwd_rows(q, k, v, e, b, h, rows, scale=None):
     S = (qq @ kk.T) * _scale(D, scale)
     M = eviction_mask(e[b], rows, n_keys)
     S = np.where(M, S, -np.inf)
-    m = S.max(axis=1, keepdims=True)
+    # a row that sees no key (only possible when a record breaks e_j > j)
+    # is an empty softmax: O = 0, LSE = -inf
+    empty = ~M.any(axis=1, keepdims=True)
+    m = np.where(empty, 0.0, S.max(axis=1, keepdims=True))
     Pu = np.exp(S - m)
     l = Pu.sum(axis=1, keepdims=True)
-    lse = (m + np.log(l))[:, 0]
-    o = (Pu / l) @ vv
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m + np.log(np.where(empty, 1.0, l)))[:, 0]
+    o = (Pu / np.where(empty, 1.0, l)) @ vv
     return o, lse
 
 
@@ -145,9 +149,10 @@ def _bwd_rows_core(q, k, v, e, do, b, h, rows, scale):
     S = (qq @ kk.T) * sc
     M = eviction_mask(e[b], rows, n_keys)
     S = np.where(M, S, -np.inf)
-    m = S.max(axis=1, keepdims=True)
+    empty = ~M.any(axis=1, keepdims=True)              # rows that see no key: P = 0
+    m = np.where(empty, 0.0, S.max(axis=1, keepdims=True))
     Pu = np.exp(S - m)
-    P = Pu / Pu.sum(axis=1, keepdims=True)            # softmax over live keys
+    P = Pu / np.where(empty, 1.0, Pu.sum(axis=1, keepdims=True))   # softmax over live keys
     dP = dd @ vv.T                                     # dP_ij = dO_i . v_j
     Di = (P * dP).sum(axis=1, keepdims=True)           # sum_j P_ij dP_ij
     dS = P * (dP - Di)

@@ -217,3 +217,57 @@ def test_bf16_raw_projection_gradients_train4k():
     gate(dk, O.rope(rdk, pos, inverse=True), "bf16grad", "dK raw")
     gate(dv, rdv, "bf16grad", "dV")
 
+
+
+def _broken_e(rng, B, N):
+    """Records that break e_j > j: a fifth of the tokens get e_j <= j (seen by
+    no query), and the first three tokens too, so rows 0..2 see no key."""
+    e = _random_e(rng, B, N)
+    j = np.arange(N)[None].repeat(B, 0)
+    bad = rng.random((B, N)) < 0.2
+    e[bad] = (j - rng.integers(0, 5, (B, N)))[bad]
+    e[:, :3] = [0, 1, 2]
+    return e
+
+
+def _empty_rows(e, N):
+    """rows that see no key under j <= i < e_j"""
+    out = []
+    for b in range(e.shape[0]):
+        vis = np.zeros(N, bool)
+        for jj in range(N):
+            vis[jj:max(jj, min(N, int(e[b, jj])))] = True
+        out.append(~vis)
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,D,seed", [(300, 8, 2, 128, 1), (129, 4, 4, 128, 2),
+                                            (200, 4, 2, 64, 3)])
+def test_bf16_broken_records(N, Hq, Hkv, D, seed):
+    """Outside the preconditions the kernels still follow the oracle's
+    reading: invisible tokens contribute nothing, rows that see no key give
+    O = 0 and LSE = -inf, and the gradients stay finite."""
+    B = 2
+    e = _broken_e(np.random.default_rng(700 + seed), B, N)
+    empty = _empty_rows(e, N)
+    assert empty[:, :3].all() and not empty.all()
+    q, k, v, do = _inputs(B, N, Hq, Hkv, D, 710 + seed, torch.bfloat16)
+    qg, kg, vg, dog, eg = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), _e_gpu(e)
+    o, lse = ks.ks_evict_attn_fwd(qg, kg, vg, eg)
+    torch.cuda.synchronize()
+    ro, rl = O.attn_fwd(f64(q), f64(k), f64(v), e)
+    gate(o, ro, "bf16", "O")
+    lg = lse.cpu().numpy()
+    for b in range(B):
+        assert np.all(np.isneginf(lg[b][:, empty[b]]))
+        assert torch.all(o[b][torch.from_numpy(empty[b]).to(DEV)] == 0)
+        gate(lse[b][:, torch.from_numpy(~empty[b]).to(DEV)], rl[b][:, ~empty[b]], "bf16", "LSE")
+    ks.ks_check_eviction_record(eg)       # counts only; exercised beside the kernels
+    if D != 128:
+        return
+    dq, dk, dv = ks.ks_evict_attn_bwd(qg, kg, vg, eg, o, lse, dog)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = O.attn_bwd(f64(q), f64(k), f64(v), e, f64(do))
+    gate(dq, rdq, "bf16grad", "dQ")
+    gate(dk, rdk, "bf16grad", "dK")
+    gate(dv, rdv, "bf16grad", "dV")

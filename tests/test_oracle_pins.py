@@ -180,6 +180,56 @@ def test_fwd_brute_force_tiny_and_exhaustive():
     np.testing.assert_allclose(lse[0, 0], lb, atol=1e-12)
 
 
+def test_broken_records_give_empty_rows():
+    """Records that break e_j > j (outside the method's preconditions): a
+    token with e_j <= j is seen by no query, and a row that sees no key is an
+    empty softmax (O = 0, LSE = -inf).  Brute force over every record with
+    e_j in {0..N} and never, for N <= 4."""
+    D = 3
+    for N in range(1, 5):
+        q, k, v = rnd((1, N, 1, D), 60 + N), rnd((1, N, 1, D), 70 + N), rnd((1, N, 1, D), 80 + N)
+        for ecomb in itertools.product(*([list(range(0, N + 1)) + [KS_NEVER]] * N)):
+            e = np.array(ecomb)[None]
+            o, lse = O.attn_fwd(q, k, v, e)
+            for i in range(N):
+                vis = [j for j in range(i + 1) if i < e[0, j]]
+                if not vis:
+                    assert np.all(o[0, i, 0] == 0) and lse[0, 0, i] == -np.inf
+                    continue
+                qs = q[0, vis, 0].copy()
+                qs[-1] = q[0, i, 0]          # the last causal row of the subset is query i
+                ob, lb = _brute_fwd(qs, k[0, vis, 0], v[0, vis, 0],
+                                    np.full(len(vis), KS_NEVER), 1 / math.sqrt(D))
+                np.testing.assert_allclose(o[0, i, 0], ob[-1], atol=1e-12)
+                np.testing.assert_allclose(lse[0, 0, i], lb[-1], atol=1e-12)
+
+
+def test_broken_record_gradients_by_finite_differences():
+    B, N, Hq, Hkv, D = 1, 16, 2, 1, 5
+    rng = np.random.default_rng(86)
+    e = random_e(rng, N)[None]
+    e[0, [0, 1, 5, 6, 9]] = [0, 1, 2, 6, 3]        # e_j <= j: rows 0 and 1 see nothing
+    q, k, v = rnd((B, N, Hq, D), 87), rnd((B, N, Hkv, D), 88), rnd((B, N, Hkv, D), 89)
+    do = rnd((B, N, Hq, D), 90)
+    o, _ = O.attn_fwd(q, k, v, e)
+    assert np.all(o[0, :2] == 0)
+    dq, dk, dv = O.attn_bwd(q, k, v, e, do)
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+    assert np.all(dq[0, :2] == 0)
+    h = 1e-6
+    pick = np.random.default_rng(91)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(20):
+            idx = tuple(int(pick.integers(0, sz)) for sz in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            fp = _loss(*(xp if n == name else args[n] for n in "qkv"), e, do)
+            fm = _loss(*(xm if n == name else args[n] for n in "qkv"), e, do)
+            assert abs((fp - fm) / (2 * h) - g[idx]) < 1e-6, (name, idx)
+
+
 def test_fwd_equals_reassembled_sequence_at_logical_positions():
     """The method's core claim: every row of the masked trace attention equals
     plain attention of that query over the re-assembled live keys, each
