@@ -271,3 +271,18 @@ def test_bf16_broken_records(N, Hq, Hkv, D, seed):
     gate(dq, rdq, "bf16grad", "dQ")
     gate(dk, rdk, "bf16grad", "dK")
     gate(dv, rdv, "bf16grad", "dV")
+
+
+def test_f32_broken_records():
+    B, N, Hq, Hkv, D = 2, 150, 2, 1, 64
+    e = _broken_e(np.random.default_rng(720), B, N)
+    empty = _empty_rows(e, N)
+    q, k, v, _ = _inputs(B, N, Hq, Hkv, D, 721, torch.float32, scale=1.0)
+    o, lse = ks.ks_evict_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), _e_gpu(e))
+    torch.cuda.synchronize()
+    ro, rl = O.attn_fwd(f64(q), f64(k), f64(v), e)
+    gate(o, ro, "f32", "O")
+    lg = lse.cpu().numpy()
+    for b in range(B):
+        assert np.all(np.isneginf(lg[b][:, empty[b]]))
+        gate(lg[b][:, ~empty[b]], rl[b][:, ~empty[b]], "f32", "LSE")
