@@ -608,12 +608,21 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
     e = tr.e[None].astype(np.int64)
     # raw projections of trace 0, kv head 0 (the generator draws whole tensors)
     bf = torch.bfloat16
-    qh = normal_tensor((1, N, Hq, D), seeds["q"], cfg.value_scale, bf, "cuda")[:, :, :G]
-    kh = normal_tensor((1, N, Hkv, D), seeds["k"], cfg.value_scale, bf, "cuda")[:, :, :1]
-    vh = normal_tensor((1, N, Hkv, D), seeds["v"], cfg.value_scale, bf, "cuda")[:, :, :1]
-    dh = normal_tensor((1, N, Hq, D), seeds["do"], cfg.value_scale, bf, "cuda")[:, :, :G]
+    qa = normal_tensor((1, N, Hq, D), seeds["q"], cfg.value_scale, bf, "cuda")
+    ka = normal_tensor((1, N, Hkv, D), seeds["k"], cfg.value_scale, bf, "cuda")
+    va = normal_tensor((1, N, Hkv, D), seeds["v"], cfg.value_scale, bf, "cuda")
+    da = normal_tensor((1, N, Hq, D), seeds["do"], cfg.value_scale, bf, "cuda")
+    qh, kh, vh, dh = qa[:, :, :G], ka[:, :, :1], va[:, :, :1], da[:, :, :G]
     f = lambda t: t.to("cpu", torch.float64).numpy()
     q, k, v, do = f(qh), f(kh), f(vh), f(dh)
+    # the GPU path on the same trace (whole trace, every head), for the error
+    # of the sampled rows against the oracle
+    import kv_cache_compaction_amd as ks
+    ks.ks_rope_logical(qa, ka, torch.arange(N, dtype=torch.int32, device="cuda")[None].contiguous())
+    eg = torch.from_numpy(tr.e[None].astype(np.int32)).cuda()
+    go, glse = ks.ks_evict_attn_fwd(qa, ka, va, eg)
+    gdq, _, _ = ks.ks_evict_attn_bwd(qa, ka, va, eg, go, glse, da)
+    torch.cuda.synchronize()
     pos = np.arange(N)[None]
     q, k = O.rope(q, pos), O.rope(k, pos)
     # prefix of the trace: rows < n only see keys < n, so the prefix is a
@@ -623,15 +632,26 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
     pairs_n = int(O.eviction_mask(en[0], np.arange(n), n).sum())
     done_pairs = 0
     heads_used = 0
+    ref = []
     t0 = time.perf_counter()
     while heads_used < G and (heads_used == 0 or time.perf_counter() - t0 < budget_s):
         h = heads_used
         qh1, doh1 = q[:, :n, h:h + 1], do[:, :n, h:h + 1]
-        O.attn_fwd(qh1, k[:, :n], v[:, :n], en)
-        O.attn_bwd(qh1, k[:, :n], v[:, :n], en, doh1)
+        ro, rl = O.attn_fwd(qh1, k[:, :n], v[:, :n], en)
+        rdq, _, _ = O.attn_bwd(qh1, k[:, :n], v[:, :n], en, doh1)
         done_pairs += pairs_n
         heads_used += 1
+        ref.append((ro, rl, rdq))
     el = time.perf_counter() - t0
+    # rows < n of the GPU's full-trace outputs against the oracle's prefix
+    err = {"o": 0.0, "lse": 0.0, "dq": 0.0}
+    scale_ref = {"o": 0.0, "lse": 0.0, "dq": 0.0}
+    for h, (ro, rl, rdq) in enumerate(ref):
+        for name, got, want in (("o", go[0, :n, h], ro[0, :, 0]), ("lse", glse[0, h, :n], rl[0, 0]),
+                                ("dq", gdq[0, :n, h], rdq[0, :, 0])):
+            g = got.to("cpu", torch.float64).numpy()
+            err[name] = max(err[name], float(np.abs(g - want).max()))
+            scale_ref[name] = max(scale_ref[name], float(np.abs(want).max()))
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     model = "unknown"
     try:
@@ -651,6 +671,11 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
         "sample": f"fp64 oracle forward + backward (dQ, dK, dV) of the first {n} tokens "
                   f"of trace 0, {heads_used} query head(s) of kv group 0: {done_pairs} live "
                   f"pairs in {el:.1f} s",
+        "gpu_vs_oracle_on_sample": {
+            "rows": n, "heads": heads_used,
+            "max_abs": {kk: round(vv, 6) for kk, vv in err.items()},
+            "max_abs_of_reference": {kk: round(vv, 4) for kk, vv in scale_ref.items()},
+        },
     }
 
 
