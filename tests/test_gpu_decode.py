@@ -213,3 +213,46 @@ def test_fused_rope_decode_against_oracle():
                             t.cpu().numpy(), L)
     gate(out, ro, "bf16", "fused decode out")
     gate(lse, rl, "bf16", "fused decode lse")
+
+
+def test_decode_step_replays_from_a_graph():
+    """The decode step (batched compaction, append, fused-rotation decode) is
+    capture-safe: a captured graph replays to the eager result every time,
+    with eager work in between (the library records no memsets)."""
+    db = build_decode_batch(np.random.default_rng(41), 6, live_range=(160, 1200), max_pos=8000)
+    B, MB = db.table0.shape
+    bf = torch.bfloat16
+    kp = normal_tensor((db.num_pool_blocks, 2, 16, 128), 4101, 0.5, bf, DEV)
+    vp = normal_tensor((db.num_pool_blocks, 2, 16, 128), 4102, 0.5, bf, DEV)
+    q = normal_tensor((B, 8, 128), 4103, 0.5, bf, DEV)
+    k4 = normal_tensor((B, 2, 128), 4104, 0.5, bf, DEV)
+    v4 = normal_tensor((B, 2, 128), 4105, 0.5, bf, DEV)
+    pos = _gpu(db.pos.astype(np.int32))
+    t0, n0, keeps = _gpu(db.table0), _gpu(db.nblk0), _gpu(db.keeps)
+    tb, nb = torch.empty_like(t0), torch.empty_like(n0)
+    seq = _gpu((db.live_len + 1).astype(np.int32))
+    out = torch.empty((B, 8, 128), dtype=bf, device=DEV)
+    lse = torch.empty((B, 8), dtype=torch.float32, device=DEV)
+    ws = torch.empty(ks.ks_paged_decode_workspace(B, 8, 128, MB), dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+
+    def step():
+        ks.ks_compact_block_table_rounds(t0, n0, keeps, tb, nb, stream=s)
+        ks.ks_append_kv(k4, v4, pos, tb, seq, kp, vp, stream=s)
+        ks.ks_paged_decode_rope(q, pos, kp, vp, tb, seq, out=out, lse=lse, ws=ws, stream=s)
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        ref_o, ref_l, ref_t = out.clone(), lse.clone(), tb.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(4):
+            out.zero_()
+            lse.zero_()
+            tb.fill_(-7)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o) and torch.equal(lse, ref_l) and torch.equal(tb, ref_t)
