@@ -9,6 +9,13 @@
  * sides: RoPE at logical positions, eviction-masked attention forward and
  * backward, block-table compaction and paged GQA decode.
  *
+ * Citations in these sources name two web pages about the method: "the
+ * explainer" is the wqu.guru article "KV-streams: accelerating agentic RL
+ * training by operating on the KV cache directly" (its paragraphs on RoPE,
+ * 16-token blocks and the block table, padding, turn-level eviction and the
+ * trainer), and "the paper page" is the thelatestinai.com summary of the
+ * paper above (abstract, Fig. 2A, Fig. 3, Tables 1-2).
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory      Every tensor pointer is DEVICE memory owned by the caller.  The
@@ -89,10 +96,10 @@ ks_status ks_rope_logical(void* q, void* k, const int32_t* pos, int B, int N,
  * ks_evict_attn_fwd -- attention over a continuous trace under the eviction
  * mask that reproduces compaction.
  *
- * The trainer replays every recorded compaction event: retained tokens keep
- * the states they formed before compaction, later tokens cannot attend spans
- * that inference had already removed (explainer, trainer paragraph; paper
- * page, Fig. 2A: "an attention mask that reproduces eviction").  With e_j the
+ * Training replays the logged compaction events: every surviving entry is
+ * the one computed when its token was generated, and a token evicted at an
+ * event is invisible to every later query (explainer, trainer paragraph;
+ * paper page, Fig. 2A, where the mask stands for the eviction).  With e_j the
  * trace index of the event that evicted token j (KS_NEVER if never):
  *   M_ij = [j <= i] and [i < e_j]
  *   LSE_i = log sum_{j: M_ij} exp(scale q_i.k_j)

@@ -2,9 +2,9 @@
 //
 // The trainer replays compaction as a mask: query i attends key j iff
 // j <= i < e_j, e_j being the trace index of the event that evicted j
-// (KV-streams explainer, trainer paragraph; paper page, Fig. 2A).  Retained
-// keys keep the states they formed before compaction simply because K and V
-// are those of the continuous trace.
+// (KV-streams explainer, trainer paragraph; paper page, Fig. 2A).  Surviving
+// keys are the ones computed during generation simply because K and V are
+// those of the continuous trace.
 //
 // Two kernels:
 //   fwd_bf16_kernel  bf16 inputs, fp32 accumulation, 32x32x16 bf16 MFMA.

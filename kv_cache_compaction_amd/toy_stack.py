@@ -5,8 +5,8 @@ attention as one eviction-masked call over the rollout, and generation runs
 token by token over paged caches that each compaction event splices
 (explainer: trainer paragraph, RoPE and block-table paragraphs).  Both
 produce next-token distributions; with the same weights they must agree up
-to rounding, because retained entries keep the states they formed before
-the event and later tokens never see the removed spans.
+to rounding, because every surviving entry is the one computed before the
+event and no later token sees a removed span.
 
 Attention, RoPE, the cache append, decode and the table splice run in
 libks; projections, norms and the MLP are plain bf16 GEMMs and elementwise

@@ -5,19 +5,22 @@ function is the plain definition, with an explicit boolean mask and no
 blocking, fusion or online softmax.
 
 Sources (the KV-streams paper, "KV-streams for Efficient Compaction in Agentic
-Reinforcement Learning", as presented on the pages):
+Reinforcement Learning", as presented on the pages): "the explainer" is the
+wqu.guru article "KV-streams: accelerating agentic RL training by operating
+on the KV cache directly"; "the paper page" is the thelatestinai.com summary
+of the paper (abstract, Fig. 2A, Fig. 3).
 
 * RoPE at logical positions: cached keys keep the rotation of their original
   position, and new queries and keys continue the original position count
-  (wqu.guru explainer, the "First, RoPE ..." paragraph and the one after it).
-* Eviction mask: the trainer replays recorded compaction events so that later
-  tokens cannot attend spans that inference had already removed, while
-  retained tokens keep the states they formed before (explainer, trainer
-  paragraph; paper page, Fig. 2A "an attention mask that reproduces
-  eviction").  Written as M_ij = [j <= i] and [i < e_j].
+  (explainer, the paragraph on RoPE after compaction and the one after it).
+* Eviction mask: training replays the logged compaction events; a token
+  evicted at an event is invisible to every query from that event on, and
+  every surviving entry is the one computed when its token was generated
+  (explainer, trainer paragraph; paper page, Fig. 2A, where the mask stands
+  for the eviction).  Written as M_ij = [j <= i] and [i < e_j].
 * Block-table compaction: remove complete 16-token blocks and join the
-  remaining block references, leaving no holes (explainer, the "Second, vLLM
-  ..." paragraph and the one after it).
+  remaining block references, leaving no holes (explainer, the paragraph on
+  vLLM's 16-token blocks and the one after it).
 * Decode: attention of the new query over the live keys gathered through the
   compacted table.
 
