@@ -115,14 +115,20 @@ ENTRY_SOURCES = {
 
 
 def kernel_sources_hash(entry: str) -> str:
-    """sha256 over the HIP sources of one entry point's kernels."""
+    """sha256 over the code of the HIP sources of one entry point's kernels
+    (comments and blank space removed, so editing a comment keeps a stored
+    counter summary valid)."""
     import hashlib
+    import re
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kv_cache_compaction_amd",
                         "csrc")
     h = hashlib.sha256()
     for name in sorted(ENTRY_SOURCES[entry]):
-        with open(os.path.join(root, name), "rb") as fh:
-            h.update(name.encode() + b"\0" + fh.read())
+        with open(os.path.join(root, name)) as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        code = " ".join(code.split())
+        h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 
