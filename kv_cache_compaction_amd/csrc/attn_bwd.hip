@@ -286,6 +286,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dva[db] = mfma32x32x16(tile_frag_t(Os, lt, 16 * ks, 32 * db), pf[ks], dva[db]);
         dka[db] = mfma32x32x16(tile_frag_t(Qs, lt, 16 * ks, 32 * db), sf[ks], dka[db]);
       }
+    // scheduling: the dO^T / Q^T transpose reads (four per MFMA pair) run
+    // three pairs ahead (0x100 = LDS reads, 0x008 = MFMA); left alone, the
+    // compiler issues them just before each MFMA, which then waits on them
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int p = 0; p < 2 * NDB; ++p) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (p < 2 * NDB - 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
   };
 
   __syncthreads();  // V staged
@@ -449,6 +458,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int ks = 0; ks < 2; ++ks)
           dqa[db] = mfma32x32x16(tile_frag_t(kv, lt, kk * 32 + 16 * ks, 32 * db), sf[ks],
                                  dqa[db]);
+      // scheduling: the K^T transpose reads (two per MFMA) run four MFMAs ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int p = 0; p < 2 * NDB; ++p) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (p < 2 * NDB - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
     }
   };
 

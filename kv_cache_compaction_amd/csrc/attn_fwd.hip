@@ -509,6 +509,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int s = 0; s < 8; ++s)
         sacc[kk] = mfma32x32x16(tile_chunk(kv, la, kk * 32, 2 * s + lh), qf[s], sacc[kk]);
     }
+    // scheduling: the K operand reads run four MFMAs ahead of their use
+    // (0x100 = LDS reads, 0x008 = MFMA; the compiler alone issues them one
+    // or two ahead and each MFMA then waits on its own read)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (p < 16 - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+
     if (partial) {  // uniform branch: element mask only on partial tiles
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -558,6 +568,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         oacc[db] = mfma32x32x16(tile_frag_t(Vt, lt, kk * 16, db * 32), pf[kk], oacc[db]);
+    // scheduling: the V^T transpose reads (two per MFMA) run six MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (p < 16 - 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
   };
 
   // live key tiles in windows of kLiveWindow; within a window, tile k is
