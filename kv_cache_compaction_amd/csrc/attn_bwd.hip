@@ -267,7 +267,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         pv[rg * 4 + 3] = fast_exp2(fmaf(sacc[rg * 4 + 3], sl2, -l4.w));
       }
     }
+    // dV MFMAs need P only: they go first, and the dS arithmetic overlaps them
     bf16x8 pf[2], sf[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)pv[r];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        dva[db] = mfma32x32x16(tile_frag_t(Os, lt, 16 * ks, 32 * db), pf[ks], dva[db]);
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const float4 d4 = *reinterpret_cast<const float4*>(Rc + BQ + rg * 8 + lh * 4);
@@ -275,25 +283,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int r = rg * 4 + c;
-        pf[r >> 3][r & 7] = (__bf16)pv[r];
         sf[r >> 3][r & 7] = (__bf16)(pv[r] * (pacc[r] - dd[c]));
       }
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        dva[db] = mfma32x32x16(tile_frag_t(Os, lt, 16 * ks, 32 * db), pf[ks], dva[db]);
+      for (int ks = 0; ks < 2; ++ks)
         dka[db] = mfma32x32x16(tile_frag_t(Qs, lt, 16 * ks, 32 * db), sf[ks], dka[db]);
-      }
-    // scheduling: the dO^T / Q^T transpose reads (four per MFMA pair) run
-    // three pairs ahead (0x100 = LDS reads, 0x008 = MFMA); left alone, the
-    // compiler issues them just before each MFMA, which then waits on them
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    // scheduling: the dO^T / Q^T transpose reads (two per MFMA) run three
+    // MFMAs ahead (0x100 = LDS reads, 0x008 = MFMA); left alone, the compiler
+    // issues them just before each MFMA, which then waits on them
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int p = 0; p < 2 * NDB; ++p) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (p < 2 * NDB - 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    for (int p = 0; p < 4 * NDB; ++p) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (p < 4 * NDB - 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
 
