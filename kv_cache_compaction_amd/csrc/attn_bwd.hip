@@ -432,15 +432,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        sacc = mfma32x32x16(tile_chunk(kv, la, kk * 32, 2 * s + lh), qf[s], sacc);
-        pacc = mfma32x32x16(tile_chunk(Vt, la, kk * 32, 2 * s + lh), gf[s], pacc);
-      }
+      // S first: its exponentials then overlap the dP MFMAs.
       // lane = query qi; accumulator row r = key j0 + 32 kk + 8 (r / 4) + 4 lh + r % 4
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s)
+        sacc = mfma32x32x16(tile_chunk(kv, la, kk * 32, 2 * s + lh), qf[s], sacc);
       float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(fmaf(sacc[r], sl2, -l2));
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s)
+        pacc = mfma32x32x16(tile_chunk(Vt, la, kk * 32, 2 * s + lh), gf[s], pacc);
       if (partial) {  // uniform branch: element mask only on partial tiles
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
