@@ -184,22 +184,22 @@ def main():
     import torch
 
     import kv_cache_compaction_amd as ks
-    from workloads import CONFIGS, build_decode_batch, config_trace_batch, normal_tensor, \
-        stacked_e
+    from workloads import (PAGED_DECODE, SUMMARY_32K, build_decode_batch, config_trace_batch,
+                           normal_tensor, stacked_e, workload_rng)
 
     dev = "cuda"
     torch.cuda.set_device(0)
     bf = torch.bfloat16
 
     # ---------------- training-side inputs (32k summary traces) ----------------
-    c3 = CONFIGS[3]
-    traces, seeds = config_trace_batch(c3)
+    trn = SUMMARY_32K
+    traces, seeds = config_trace_batch(trn)
     e_np = stacked_e(traces)
-    B, N, Hq, Hkv, D = c3.batch, c3.N, c3.Hq, c3.Hkv, c3.D
-    q = normal_tensor((B, N, Hq, D), seeds["q"], c3.value_scale, bf, dev)
-    k = normal_tensor((B, N, Hkv, D), seeds["k"], c3.value_scale, bf, dev)
-    v = normal_tensor((B, N, Hkv, D), seeds["v"], c3.value_scale, bf, dev)
-    do = normal_tensor((B, N, Hq, D), seeds["do"], c3.value_scale, bf, dev)
+    B, N, Hq, Hkv, D = trn.batch, trn.N, trn.Hq, trn.Hkv, trn.D
+    q = normal_tensor((B, N, Hq, D), seeds["q"], trn.value_scale, bf, dev)
+    k = normal_tensor((B, N, Hkv, D), seeds["k"], trn.value_scale, bf, dev)
+    v = normal_tensor((B, N, Hkv, D), seeds["v"], trn.value_scale, bf, dev)
+    do = normal_tensor((B, N, Hq, D), seeds["do"], trn.value_scale, bf, dev)
     e = torch.from_numpy(e_np).to(dev)
     pos = torch.arange(N, dtype=torch.int32, device=dev)[None].repeat(B, 1).contiguous()
     o = torch.empty_like(q)
@@ -217,16 +217,16 @@ def main():
     causal_pairs = B * N * (N + 1) // 2
 
     # ---------------- inference-side inputs (paged decode) ----------------
-    c4 = CONFIGS[4]
-    db = build_decode_batch(np.random.default_rng(1000 + 4), c4.batch)
+    dec = PAGED_DECODE
+    db = build_decode_batch(workload_rng(dec), dec.batch)
     DB, MB = db.table0.shape
     NB = db.num_pool_blocks
-    H4q, H4kv = c4.Hq, c4.Hkv
-    kp = normal_tensor((NB, H4kv, 16, D), 4001, 0.5, bf, dev)
-    vp = normal_tensor((NB, H4kv, 16, D), 4002, 0.5, bf, dev)
-    q4 = normal_tensor((DB, 1, H4q, D), 4003, 0.5, bf, dev)
-    k4 = normal_tensor((DB, H4kv, D), 4004, 0.5, bf, dev)
-    v4 = normal_tensor((DB, H4kv, D), 4005, 0.5, bf, dev)
+    Hq_d, Hkv_d = dec.Hq, dec.Hkv
+    kp = normal_tensor((NB, Hkv_d, 16, D), 4001, 0.5, bf, dev)
+    vp = normal_tensor((NB, Hkv_d, 16, D), 4002, 0.5, bf, dev)
+    q4 = normal_tensor((DB, 1, Hq_d, D), 4003, 0.5, bf, dev)
+    k4 = normal_tensor((DB, Hkv_d, D), 4004, 0.5, bf, dev)
+    v4 = normal_tensor((DB, Hkv_d, D), 4005, 0.5, bf, dev)
     pos4 = torch.from_numpy(db.pos[:, None].astype(np.int32)).to(dev)
     pos4f = pos4[:, 0].contiguous()
     table0 = torch.from_numpy(db.table0).to(dev)
@@ -235,16 +235,16 @@ def main():
     tbufs = [torch.empty_like(table0), torch.empty_like(table0)]
     nbufs = [torch.empty_like(nblk0), torch.empty_like(nblk0)]
     seq_lens = torch.from_numpy((db.live_len + 1).astype(np.int32)).to(dev)
-    out4 = torch.empty((DB, H4q, D), dtype=bf, device=dev)
-    lse4 = torch.empty((DB, H4q), dtype=torch.float32, device=dev)
-    ws_d = torch.empty(ks.ks_paged_decode_workspace(DB, H4q, D, MB), dtype=torch.uint8,
+    out4 = torch.empty((DB, Hq_d, D), dtype=bf, device=dev)
+    lse4 = torch.empty((DB, Hq_d), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(ks.ks_paged_decode_workspace(DB, Hq_d, D, MB), dtype=torch.uint8,
                        device=dev)
     L = db.live_len.astype(np.int64) + 1
     # decode step bytes: K/V of every live token once, q (read once, rotated
     # in the kernel), the appended token's k/v (read + write), output, lse,
     # table entries and lengths
-    dec_bytes = int((L * H4kv * D * 2 * 2).sum()) + DB * H4q * D * 2 + \
-        2 * 2 * DB * H4kv * D * 2 + DB * H4q * D * 2 + DB * H4q * 4 + \
+    dec_bytes = int((L * Hkv_d * D * 2 * 2).sum()) + DB * Hq_d * D * 2 + \
+        2 * 2 * DB * Hkv_d * D * 2 + DB * Hq_d * D * 2 + DB * Hq_d * 4 + \
         int(((L + 15) // 16).sum()) * 4 + DB * 4
     # compaction bytes: the table rows and every event's keep flags read once,
     # the compacted rows and lengths written once
@@ -397,24 +397,26 @@ def main():
                    for kk, vv in parts.items()},
     }
     result["hbm_reference"] = hbm_reference(torch, stream)
-    result["single_token_blocks"] = token_granular_decode(ks, torch, stream, c4)
+    result["single_token_blocks"] = token_granular_decode(ks, torch, stream, dec)
     result["toy_stack"] = toy_stack_mismatch(torch)
     result["reprefill_counterfactual"] = reprefill_counterfactual(
-        ks, torch, traces, q, k, v, do, stream, ms, pairs, c3)
+        ks, torch, traces, q, k, v, do, stream, ms, pairs, trn)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(traces, seeds, c3, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(traces, seeds, trn, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
 def hbm_reference(torch, stream, nbytes=2 << 30, reps=5):
     """What plain library kernels reach on this GPU's HBM, as context for the
     decode and compaction figures: a device-to-device copy (read + write) and
-    a full read (a sum over fp32) of 2 GiB."""
+    a full read of 2 GiB (fp32 sums of 4096 rows, the fastest of torch's
+    reductions here; a flat sum to one value reads at about two thirds of it)."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    rows = src.view(4096, -1)
     out = {}
     for name, fn, traffic in (("copy", lambda: dst.copy_(src), 2 * nbytes),
-                              ("read", lambda: src.sum(), nbytes)):
+                              ("read", lambda: rows.sum(dim=1), nbytes)):
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -434,9 +436,9 @@ def token_granular_decode(ks, torch, stream, cfg, reps=5):
     tables (all events in one launch, rows of up to 65k entries), then RoPE of q,
     append of the new token and the decode.  Timed apart from the step; HBM
     bytes as for the 16-token decode, with one table entry per token."""
-    from workloads import build_decode_batch, normal_tensor
+    from workloads import build_decode_batch, normal_tensor, workload_rng
 
-    db = build_decode_batch(np.random.default_rng(1000 + 4), cfg.batch, block=1)
+    db = build_decode_batch(workload_rng(cfg), cfg.batch, block=1)
     B, MT = db.table0.shape
     NT = db.num_pool_blocks
     Hq, Hkv, D = cfg.Hq, cfg.Hkv, cfg.D

@@ -9,7 +9,7 @@ import torch
 import kv_cache_compaction_amd as ks
 import oracle as O
 from parity_util import announce, errors, f64, gate, passes
-from workloads import CONFIGS, KS_NEVER, config_trace_batch, normal_tensor, stacked_e
+from workloads import KS_NEVER, TINY_F32, TRAIN_4K, config_trace_batch, normal_tensor, stacked_e
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -43,7 +43,7 @@ def _inputs(B, N, Hq, Hkv, D, seed, dtype, scale=0.5):
 
 # ---------------------------------------------------------------------------
 def test_tiny512_f32_rope_then_forward():
-    cfg = CONFIGS[1]
+    cfg = TINY_F32
     (tr,), seeds = config_trace_batch(cfg)
     B, N, D = 1, cfg.N, cfg.D
     q = normal_tensor((B, N, 1, D), seeds["q"])
@@ -77,7 +77,7 @@ def test_f32_forward_random_masks(N, G, seed):
 # ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def train4k():
-    cfg = CONFIGS[2]
+    cfg = TRAIN_4K
     traces, seeds = config_trace_batch(cfg)
     e = stacked_e(traces)
     B, N = cfg.batch, cfg.N
@@ -178,7 +178,7 @@ def test_bf16_diagonal_only_and_causal():
 def test_bf16_end_to_end_rope_train4k():
     """RoPE at logical positions then the masked forward, against the oracle
     doing both in fp64 from the same raw projections."""
-    cfg = CONFIGS[2]
+    cfg = TRAIN_4K
     traces, seeds = config_trace_batch(cfg)
     e = stacked_e(traces)
     B, N = cfg.batch, cfg.N
@@ -198,7 +198,7 @@ def test_bf16_raw_projection_gradients_train4k():
     forward and backward on the GPU, then the inverse rotation of dQ, dK
     (ks_rope_logical with inverse), against the oracle's gradients through
     its own RoPE."""
-    cfg = CONFIGS[2]
+    cfg = TRAIN_4K
     traces, seeds = config_trace_batch(cfg)
     e = stacked_e(traces)
     B, N = cfg.batch, cfg.N

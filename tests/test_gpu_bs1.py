@@ -12,7 +12,8 @@ import torch
 import kv_cache_compaction_amd as ks
 import oracle as O
 from parity_util import announce, f64, gate
-from workloads import CONFIGS, KS_NEVER, build_decode_batch, build_trace, check_trace, normal_tensor
+from workloads import (KS_NEVER, PAGED_DECODE, TRAIN_4K, build_decode_batch, build_trace,
+                       check_trace, normal_tensor, workload_rng)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -105,7 +106,7 @@ def test_compact_rounds_long_rows(B, MB, R, seed, with_pos):
 
 
 def test_compact_rounds_token_batch():
-    db = build_decode_batch(np.random.default_rng(1000 + 4), 64, block=1)
+    db = build_decode_batch(workload_rng(PAGED_DECODE), 64, block=1)
     out, n, _ = ks.ks_compact_block_table_rounds(_gpu(db.table0), _gpu(db.nblk0),
                                                  _gpu(db.keeps))
     torch.cuda.synchronize()
@@ -197,8 +198,8 @@ def test_token_granular_batch_full_size():
     tokens at any length, 1-6 token-run events compacted one call per event
     (rows of up to 65k entries), RoPE of q, append of the new token, decode.
     Tables bit-exact; outputs of 8 sampled sequences against the oracle."""
-    cfg = CONFIGS[4]
-    db = build_decode_batch(np.random.default_rng(1000 + 4), cfg.batch, block=1)
+    cfg = PAGED_DECODE
+    db = build_decode_batch(workload_rng(PAGED_DECODE), cfg.batch, block=1)
     B, MT = db.table0.shape
     NT = db.num_pool_blocks
     Hq, Hkv, D = cfg.Hq, cfg.Hkv, cfg.D
@@ -247,7 +248,7 @@ def test_token_granular_batch_full_size():
 # training on an unpadded (token-granular) trace
 # ---------------------------------------------------------------------------
 def test_masked_attention_on_token_granular_trace():
-    cfg = CONFIGS[2]
+    cfg = TRAIN_4K
     rng = np.random.default_rng(2222)
     tr = build_trace(rng, cfg.N, cfg.P + 5, cfg.budget, "recent", turn_len=(37, 301),
                      granule=1)

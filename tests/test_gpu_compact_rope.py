@@ -7,8 +7,8 @@ import torch
 import kv_cache_compaction_amd as ks
 import oracle as O
 from parity_util import announce, f64
-from workloads import CONFIGS, build_decode_batch, config_trace_batch, normal_tensor, \
-    trace_blocks_keep
+from workloads import (PAGED_DECODE, TINY_F32, build_decode_batch, config_trace_batch,
+                       normal_tensor, trace_blocks_keep, workload_rng)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -25,7 +25,7 @@ def _gpu(a, dtype=None):
 
 
 def test_compact_tiny512_table():
-    (tr,), _ = config_trace_batch(CONFIGS[1])
+    (tr,), _ = config_trace_batch(TINY_F32)
     perm = np.random.default_rng(7).permutation(32).astype(np.int32)[None]
     keep = trace_blocks_keep(tr)[None]
     nblk = np.array([32], np.int32)
@@ -37,7 +37,7 @@ def test_compact_tiny512_table():
 
 
 def test_compact_decode64_rounds_pingpong():
-    db = build_decode_batch(np.random.default_rng(1004), 64)
+    db = build_decode_batch(workload_rng(PAGED_DECODE), 64)
     B, MB = db.table0.shape
     ta, tb = _gpu(db.table0), torch.empty((B, MB), dtype=torch.int32, device=DEV)
     na, nb = _gpu(db.nblk0), torch.empty(B, dtype=torch.int32, device=DEV)
@@ -76,7 +76,7 @@ def _oracle_rounds(table, nblk, keeps, pos=None):
 
 def test_compact_rounds_decode64_one_launch():
     """All events of the decode workload in one launch equal the event-by-event oracle."""
-    db = build_decode_batch(np.random.default_rng(1004), 64)
+    db = build_decode_batch(workload_rng(PAGED_DECODE), 64)
     B, MB = db.table0.shape
     pos0 = np.tile(np.arange(MB, dtype=np.int32), (B, 1))
     out, n, pos = ks.ks_compact_block_table_rounds(_gpu(db.table0), _gpu(db.nblk0),

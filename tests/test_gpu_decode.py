@@ -8,7 +8,7 @@ import torch
 import kv_cache_compaction_amd as ks
 import oracle as O
 from parity_util import announce, f64, gate
-from workloads import CONFIGS, build_decode_batch, normal_tensor
+from workloads import PAGED_DECODE, build_decode_batch, normal_tensor, workload_rng
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -80,8 +80,8 @@ def run_decode_case(db, Hq, Hkv, D=128, seed=0, poison=True, base=10000.0):
 
 
 def test_decode64_full_compaction_then_decode():
-    cfg = CONFIGS[4]
-    db = build_decode_batch(np.random.default_rng(1000 + 4), cfg.batch)
+    cfg = PAGED_DECODE
+    db = build_decode_batch(workload_rng(PAGED_DECODE), cfg.batch)
     out, lse, ro, rl = run_decode_case(db, cfg.Hq, cfg.Hkv, seed=4000)
     gate(out, ro, "bf16", "decode out")
     gate(lse, rl, "bf16", "decode lse")
@@ -172,7 +172,7 @@ def test_fused_rope_decode_equals_rope_then_decode(block):
     """ks_paged_decode_rope on the unrotated query equals ks_rope_logical then
     the decode, bit for bit, on the 64-sequence batch (16-token and
     single-token blocks); the query is left unrotated."""
-    db = build_decode_batch(np.random.default_rng(1000 + 4), 64, block=block)
+    db = build_decode_batch(workload_rng(PAGED_DECODE), 64, block=block)
     B, MB = db.table0.shape
     Hq, Hkv, D = 32, 8, 128
     shape = (db.num_pool_blocks, Hkv, 16, D) if block == 16 else (db.num_pool_blocks, Hkv, D)

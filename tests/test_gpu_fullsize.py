@@ -8,7 +8,7 @@ import torch
 import kv_cache_compaction_amd as ks
 import oracle as O
 from parity_util import announce, f64, gate
-from workloads import CONFIGS, config_trace_batch, normal_tensor, stacked_e
+from workloads import SUMMARY_32K, config_trace_batch, normal_tensor, stacked_e
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -87,4 +87,4 @@ def test_summary_32k_sampled():
         t1 = tr.events[0]
         return [np.arange(tr.N - 64, tr.N),                      # queries [j, N)
                 np.arange(t1 - 1536 - 64, t1 - 1536)]            # evicted at t1
-    run_training_config(CONFIGS[3], b=1, hkv=3, key_blocks=key_blocks)
+    run_training_config(SUMMARY_32K, b=1, hkv=3, key_blocks=key_blocks)

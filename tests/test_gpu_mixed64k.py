@@ -10,12 +10,12 @@ import torch
 import kv_cache_compaction_amd as ks
 import oracle as O
 from parity_util import announce, f64, gate
-from workloads import (BLOCK, CONFIGS, KS_NEVER, config_trace_batch, evict_units,
+from workloads import (BLOCK, KS_NEVER, LONG_MIXED_64K, config_trace_batch, evict_units,
                        normal_tensor, stacked_e)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-CFG = CONFIGS[5]
+CFG = LONG_MIXED_64K
 NDEC = 256
 EVENT_AFTER = 128
 

@@ -10,8 +10,8 @@ import torch
 import kv_cache_compaction_amd as ks
 import oracle as O
 from parity_util import announce, f64, gate
-from workloads import CONFIGS, config_trace_batch, normal_tensor, reprefill_pack, \
-    reprefill_segments
+from workloads import (SUMMARY_32K, TRAIN_4K, config_trace_batch, normal_tensor, reprefill_pack,
+                       reprefill_segments)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -39,7 +39,7 @@ def _packed_inputs(cfg, pad_to=None):
 
 
 def test_reprefill_4k_full_parity():
-    cfg = CONFIGS[2]
+    cfg = TRAIN_4K
     traces, packs, e, x = _packed_inputs(cfg)
     assert len(reprefill_segments(traces[0])) >= 2
     o, lse = ks.ks_evict_attn_fwd(x["q"], x["k"], x["v"], e)
@@ -62,7 +62,7 @@ def test_reprefill_4k_full_parity():
 
 def test_reprefill_32k_sampled():
     """The bench's packed launch (4 traces padded to a common length)."""
-    cfg = CONFIGS[3]
+    cfg = SUMMARY_32K
     traces, packs, e, x = _packed_inputs(cfg)
     o, lse = ks.ks_evict_attn_fwd(x["q"], x["k"], x["v"], e)
     dq, dk, dv = ks.ks_evict_attn_bwd(x["q"], x["k"], x["v"], e, o, lse, x["do"])

@@ -15,8 +15,9 @@ import pytest
 import torch
 
 import oracle as O
-from workloads import (CONFIGS, KS_NEVER, build_decode_batch, build_trace,
-                       check_trace, config_trace_batch, trace_blocks_keep)
+from workloads import (KS_NEVER, PAGED_DECODE, SUMMARY_32K, TINY_F32, TRAINING_WORKLOADS,
+                       build_decode_batch, build_trace, check_trace, config_trace_batch,
+                       trace_blocks_keep, workload_rng)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -427,7 +428,7 @@ def test_compaction_rounds_equal_union_and_conserve_tokens():
 def test_tiny512_worked_example():
     with open(os.path.join(GOLDEN, "tiny512_trace.json")) as f:
         g = json.load(f)
-    (tr,), _ = config_trace_batch(CONFIGS[1])
+    (tr,), _ = config_trace_batch(TINY_F32)
     assert tr.events == g["events"]
     e = tr.e.astype(np.int64)
     for t, spans in g["evicted"].items():
@@ -505,18 +506,17 @@ def test_decode_no_evictions_is_last_causal_row():
 # Generator invariants (inputs shared by both sides)
 # ---------------------------------------------------------------------------
 def test_generator_invariants_all_configs():
-    for c in (1, 2, 3, 5):
-        cfg = CONFIGS[c]
+    for cfg in TRAINING_WORKLOADS:
         traces, _ = config_trace_batch(cfg)      # runs check_trace on each
         assert len(traces) == cfg.batch
-    (t3, *_), _ = config_trace_batch(CONFIGS[3])
+    (t3, *_), _ = config_trace_batch(SUMMARY_32K)
     # re-prefill factor N/(B-(o+s)) of the paper's Fig. 3: 32768/6656 = 4.92
     assert abs(32768 / (8192 - 1536) - 4.92) < 0.01
     assert len(t3.events) == 5
 
 
 def test_decode_batch_structure():
-    db = build_decode_batch(np.random.default_rng(1004), 64)
+    db = build_decode_batch(workload_rng(PAGED_DECODE), 64)
     assert np.all(db.live_len % 16 == 0) and np.all(db.pos % 16 == 0)
     assert db.live_len.min() >= 4096 and db.live_len.max() <= 16384
     assert db.pos.max() <= 65536
@@ -584,7 +584,7 @@ def test_decode_single_token_blocks_equal_16_token_blocks():
 
 
 def test_token_decode_batch_structure():
-    db = build_decode_batch(np.random.default_rng(1004), 64, block=1)
+    db = build_decode_batch(workload_rng(PAGED_DECODE), 64, block=1)
     assert db.block == 1 and np.any(db.live_len % 16) and np.any(db.pos % 16)
     assert db.live_len.min() >= 4096 and db.live_len.max() <= 16384
     ids = np.concatenate([db.table0[b, :db.nblk0[b]] for b in range(64)])

@@ -3,12 +3,13 @@ Fig. 3): structure pinned on the CPU against what the pages state and the
 trace rules imply."""
 import numpy as np
 
-from workloads import CONFIGS, KS_NEVER, config_trace_batch, reprefill_segments
+from workloads import (KS_NEVER, SUMMARY_32K, TINY_F32, TRAINING_WORKLOADS, TRAIN_4K,
+                       config_trace_batch, reprefill_segments)
 
 
 def test_segments_cover_the_rollout_once_and_respect_the_budget():
-    for k in (1, 2, 3, 5):
-        traces, _ = config_trace_batch(CONFIGS[k])
+    for cfg in TRAINING_WORKLOADS:
+        traces, _ = config_trace_batch(cfg)
         for tr in traces:
             segs = reprefill_segments(tr)
             assert len(segs) == len(tr.events) + 1
@@ -28,7 +29,7 @@ def test_segments_cover_the_rollout_once_and_respect_the_budget():
 
 
 def test_summary_retains_prompt_plus_overlap_and_summary():
-    traces, _ = config_trace_batch(CONFIGS[3])
+    traces, _ = config_trace_batch(SUMMARY_32K)
     for tr in traces:
         segs = reprefill_segments(tr)
         for s, t in zip(segs[1:], tr.events):
@@ -42,7 +43,7 @@ def test_reprocessing_factor_matches_fig3():
     """Fig. 3: each kept token is re-processed about N / (B - (o+s)) times;
     the 32k summary traces give 5 events for a factor of 32768/6656 = 4.92,
     and the extra re-prefilled tokens are events x (P + o + s)."""
-    traces, _ = config_trace_batch(CONFIGS[3])
+    traces, _ = config_trace_batch(SUMMARY_32K)
     for tr in traces:
         factor = tr.N / (tr.budget - (tr.overlap + tr.summary))
         assert abs(len(tr.events) - factor) < 1.0
@@ -51,7 +52,7 @@ def test_reprocessing_factor_matches_fig3():
 
 
 def test_no_event_means_one_segment():
-    traces, _ = config_trace_batch(CONFIGS[1])
+    traces, _ = config_trace_batch(TINY_F32)
     tr = traces[0]
     import dataclasses
     flat = dataclasses.replace(tr, events=[], e=np.full(tr.N, KS_NEVER, np.int32))
@@ -110,7 +111,7 @@ def test_packed_sequence_is_the_separate_causal_passes():
 def test_pack_rejects_short_length():
     import pytest as _pt
     from workloads import reprefill_pack
-    traces, _ = config_trace_batch(CONFIGS[2])
+    traces, _ = config_trace_batch(TRAIN_4K)
     n = sum(len(x) for x in reprefill_segments(traces[0]))
     with _pt.raises(ValueError):
         reprefill_pack(traces[0], length=n - 1)

@@ -12,5 +12,7 @@ from .traces import (  # noqa: F401
     build_decode_batch, normal_tensor, reprefill_pack, reprefill_segments,
     trace_blocks_keep,
 )
-from .configs import CONFIGS, Config, config_trace_batch, stacked_e  # noqa: F401
+from .configs import (LONG_MIXED_64K, PAGED_DECODE, SUMMARY_32K, TINY_F32,  # noqa: F401
+                      TRAIN_4K, TRAINING_WORKLOADS, WORKLOADS, Config, config_trace_batch,
+                      stacked_e, workload_rng)
 from .toy import ToyShape, toy_tokens, toy_weights  # noqa: F401

@@ -1,9 +1,10 @@
 """The five workload configurations of the KV-streams hot path.
 
-Seeds: configuration ``k`` (1-based) draws its structure from
-``numpy.random.default_rng(1000 + k)``; trace ``b`` of a batch uses child ``b``
-of ``default_rng(1000 + k).spawn(...)``.  Tensor seeds are drawn from the same
-generator, so every input is a pure function of the configuration number.
+Seeds: a configuration with seed index ``k`` draws its structure from
+``numpy.random.default_rng(1000 + k)`` (``workload_rng``); trace ``b`` of a
+batch uses child ``b`` of that generator's ``spawn(...)``.  Tensor seeds are
+drawn from the same generator, so every input is a pure function of the seed
+index.
 
 The shapes stand in for the paper's rollouts (32k-token rollouts, budgets B
 and overlap/summary sizes o+s: paper page, Fig. 3; 16-padded turns: wqu.guru
@@ -21,7 +22,7 @@ from .traces import build_trace, check_trace
 
 @dataclass(frozen=True)
 class Config:
-    idx: int
+    seed_index: int
     name: str
     batch: int
     N: int
@@ -40,22 +41,29 @@ class Config:
     rope_base: float = 10000.0
 
 
-CONFIGS = {
-    1: Config(1, "tiny-f32", batch=1, N=512, Hq=1, Hkv=1, D=64, dtype="f32",
+TINY_F32 = Config(1, "tiny-f32", batch=1, N=512, Hq=1, Hkv=1, D=64, dtype="f32",
               P=64, budget=256, strategies=("recent",), turn_len=(64, 64),
-              value_scale=1.0, backward=False),
-    2: Config(2, "train-4k", batch=1, N=4096, Hq=8, Hkv=2, D=128, dtype="bf16",
-              P=256, budget=2048, strategies=("recent",)),
-    3: Config(3, "summary-32k", batch=4, N=32768, Hq=32, Hkv=8, D=128,
+              value_scale=1.0, backward=False)
+TRAIN_4K = Config(2, "train-4k", batch=1, N=4096, Hq=8, Hkv=2, D=128, dtype="bf16",
+              P=256, budget=2048, strategies=("recent",))
+SUMMARY_32K = Config(3, "summary-32k", batch=4, N=32768, Hq=32, Hkv=8, D=128,
               dtype="bf16", P=512, budget=8192, strategies=("summary",),
-              overlap=1024, summary=512),
-    4: Config(4, "paged-decode", batch=64, N=0, Hq=32, Hkv=8, D=128,
-              dtype="bf16", P=16, budget=0, strategies=(), backward=False),
-    5: Config(5, "long-mixed-64k", batch=8, N=65536, Hq=64, Hkv=8, D=128,
+              overlap=1024, summary=512)
+PAGED_DECODE = Config(4, "paged-decode", batch=64, N=0, Hq=32, Hkv=8, D=128,
+              dtype="bf16", P=16, budget=0, strategies=(), backward=False)
+LONG_MIXED_64K = Config(5, "long-mixed-64k", batch=8, N=65536, Hq=64, Hkv=8, D=128,
               dtype="bf16", P=512, budget=16384,
               strategies=("window", "recent", "summary"),
-              overlap=2048, summary=1024),
-}
+              overlap=2048, summary=1024)
+
+# every workload by name; the training ones (those with traces) in order of size
+WORKLOADS = {c.name: c for c in (TINY_F32, TRAIN_4K, SUMMARY_32K, PAGED_DECODE, LONG_MIXED_64K)}
+TRAINING_WORKLOADS = (TINY_F32, TRAIN_4K, SUMMARY_32K, LONG_MIXED_64K)
+
+
+def workload_rng(cfg: Config) -> np.random.Generator:
+    """The generator a configuration's structure is drawn from."""
+    return np.random.default_rng(1000 + cfg.seed_index)
 
 
 def config_trace_batch(cfg: Config, check: bool = True):
@@ -64,7 +72,7 @@ def config_trace_batch(cfg: Config, check: bool = True):
     Returns ``(traces, seeds)`` where ``seeds`` maps the tensor names
     q, k, v, do to integer seeds.
     """
-    root = np.random.default_rng(1000 + cfg.idx)
+    root = workload_rng(cfg)
     seeds = {name: int(root.integers(0, 2**31 - 1)) for name in ("q", "k", "v", "do")}
     children = root.spawn(cfg.batch)
     traces = []
