@@ -557,9 +557,7 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
     return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_bwd: only bf16 with D=128 (dtype=%d D=%d)",
                    dtype, Dh);
   const int G = Hq / Hkv;
-  const int hpw = G >= 4 ? 4 : G;
-  if (G % hpw != 0)
-    return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_bwd: group size %d unsupported", G);
+  const int hpw = ks_heads_per_wave(G);
   if (B == 0 || N == 0) return KS_OK;
   KS_REQUIRE(q && k && v && e && o && lse && dout && dq && dk && dv,
              "ks_evict_attn_bwd: null pointer");

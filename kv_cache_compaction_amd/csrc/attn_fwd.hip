@@ -656,9 +656,7 @@ extern "C" ks_status ks_evict_attn_fwd(const void* q, const void* k, const void*
     return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_fwd: bf16 needs D=64 or 128 (D=%d)", D);
   if (dtype == KS_F32 && !(D == 64 || D == 128))
     return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_fwd: f32 needs D=64 or 128 (D=%d)", D);
-  const int hpw = G >= 4 ? 4 : G;
-  if (dtype == KS_BF16 && G % hpw != 0)
-    return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_fwd: group size %d unsupported", G);
+  const int hpw = ks_heads_per_wave(G);
   if (B == 0 || N == 0) return KS_OK;
   KS_REQUIRE(q && k && v && e && o, "ks_evict_attn_fwd: null pointer");
   KS_REQUIRE(ks_aligned16(q) && ks_aligned16(k) && ks_aligned16(v) && ks_aligned16(o),

@@ -348,8 +348,7 @@ ks_status decode_impl(const char* name, const void* q, const void* k_pool, const
     return ks_fail(KS_ERR_UNSUPPORTED, "%s: only bf16 with D=128 (got dtype=%d D=%d)", name,
                    dtype, Dh);
   const int G = Hq / Hkv;
-  const int hpw = G >= 4 ? 4 : G;
-  if (G % hpw != 0) return ks_fail(KS_ERR_UNSUPPORTED, "%s: group size %d unsupported", name, G);
+  const int hpw = ks_heads_per_wave(G);
   if (B == 0) return KS_OK;
   KS_REQUIRE(q && k_pool && v_pool && table && seq_lens && out, "%s: null pointer", name);
   KS_REQUIRE(ks_aligned16(q) && ks_aligned16(k_pool) && ks_aligned16(v_pool) && ks_aligned16(out),

@@ -30,6 +30,11 @@ static inline bool ks_aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// Query heads per wave in the GQA kernels: the largest of 4, 2, 1 that
+// divides the group size G = Hq / Hkv, so the heads of one wave always share
+// one kv head (the kernels are instantiated for these three values only).
+static inline int ks_heads_per_wave(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+
 // ---------------------------------------------------------------------------
 // device helpers
 // ---------------------------------------------------------------------------

@@ -123,7 +123,9 @@ def test_train4k_negative_controls(train4k):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("N,Hq,Hkv,D,seed", [
     (1, 4, 1, 128, 1), (65, 4, 4, 128, 2), (300, 8, 2, 128, 3), (517, 8, 1, 128, 4),
-    (700, 2, 1, 128, 5), (450, 4, 2, 64, 6), (129, 16, 2, 128, 7)])
+    (700, 2, 1, 128, 5), (450, 4, 2, 64, 6), (129, 16, 2, 128, 7),
+    # group sizes 3 and 6: one and two query heads per wave
+    (150, 6, 2, 128, 8), (140, 12, 2, 128, 9), (90, 3, 1, 64, 10), (77, 12, 2, 64, 11)])
 def test_bf16_forward_random_masks(N, Hq, Hkv, D, seed):
     B = 2
     rng = np.random.default_rng(seed)
@@ -138,7 +140,7 @@ def test_bf16_forward_random_masks(N, Hq, Hkv, D, seed):
 
 @pytest.mark.parametrize("N,Hq,Hkv,seed", [
     (1, 4, 1, 1), (70, 4, 4, 2), (300, 8, 2, 3), (517, 8, 1, 4), (260, 2, 1, 5),
-    (129, 16, 2, 6)])
+    (129, 16, 2, 6), (150, 6, 2, 7), (140, 12, 2, 8)])
 def test_bf16_backward_random_masks(N, Hq, Hkv, seed):
     B, D = 2, 128
     rng = np.random.default_rng(seed)

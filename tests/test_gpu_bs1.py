@@ -141,7 +141,8 @@ def _direct_bs1(B, Hq, Hkv, lens, seed, extra=7):
     return q, kp, vp, table
 
 
-@pytest.mark.parametrize("Hq,Hkv,seed", [(32, 8, 1), (8, 4, 2), (4, 4, 3)])
+@pytest.mark.parametrize("Hq,Hkv,seed", [(32, 8, 1), (8, 4, 2), (4, 4, 3), (12, 4, 4),
+                                         (12, 2, 5)])
 def test_decode_bs1_ragged_lengths(Hq, Hkv, seed):
     # 768 = one split of 48 groups of 16 tokens
     lens = np.array([0, 1, 15, 16, 17, 767, 768, 769, 1537, 3001], np.int32)

@@ -87,7 +87,10 @@ def test_decode64_full_compaction_then_decode():
     gate(lse, rl, "bf16", "decode lse")
 
 
-@pytest.mark.parametrize("Hq,Hkv,seed", [(32, 8, 1), (64, 8, 2), (8, 4, 3), (4, 4, 4)])
+# group sizes 4, 8, 2, 1, and 3 and 6 (neither a multiple of 4: two or one
+# query heads per wave)
+@pytest.mark.parametrize("Hq,Hkv,seed", [(32, 8, 1), (64, 8, 2), (8, 4, 3), (4, 4, 4),
+                                         (6, 2, 5), (24, 4, 6)])
 def test_small_batches_group_sizes(Hq, Hkv, seed):
     db = build_decode_batch(np.random.default_rng(seed), 5, live_range=(160, 1200),
                             max_pos=4096)
