@@ -118,9 +118,19 @@ def _cuda_contig(name, t, dtype=None):
         _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _given(name, t, shape, dtype):
+    """A caller-supplied output: a contiguous GPU tensor of exactly this shape
+    and dtype (the library writes through the raw pointer, so a smaller or
+    strided buffer would be written past its end)."""
+    _cuda_contig(name, t, dtype)
+    _need(tuple(t.shape) == tuple(shape), f"{name} must be {list(shape)}, got {list(t.shape)}")
+    return t
+
+
 def _workspace(nbytes, device, ws):
     if ws is None:
         return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    _cuda_contig("ws", ws)
     _need(ws.numel() * ws.element_size() >= nbytes, "workspace too small")
     return ws
 
@@ -161,12 +171,9 @@ def ks_evict_attn_fwd(q, k, v, e, scale=None, out=None, lse=None, ws=None, strea
     _cuda_contig("e", e, torch.int32)
     _need(tuple(k.shape) == (B, N, Hkv, D) and tuple(v.shape) == (B, N, Hkv, D), "k/v shape")
     _need(tuple(e.shape) == (B, N), "e must be [B, N]")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    _cuda_contig("out", out, q.dtype)
-    _cuda_contig("lse", lse, torch.float32)
+    out = torch.empty_like(q) if out is None else _given("out", out, q.shape, q.dtype)
+    lse = (torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None
+           else _given("lse", lse, (B, Hq, N), torch.float32))
     code = _dtype_code(q)
     nbytes = lib.ks_evict_attn_fwd_workspace(B, N, Hq, Hkv, D, code)
     ws = _workspace(nbytes, q.device, ws)
@@ -192,11 +199,13 @@ def ks_evict_attn_bwd(q, k, v, e, o, lse, dout, scale=None, dq=None, dk=None, dv
         _cuda_contig(name, t, q.dtype)
     _cuda_contig("e", e, torch.int32)
     _cuda_contig("lse", lse, torch.float32)
+    _need(tuple(k.shape) == (B, N, Hkv, D) and tuple(v.shape) == (B, N, Hkv, D), "k/v shape")
+    _need(tuple(e.shape) == (B, N), "e must be [B, N]")
     _need(tuple(o.shape) == tuple(q.shape) and tuple(dout.shape) == tuple(q.shape), "o/dout")
     _need(tuple(lse.shape) == (B, Hq, N), "lse must be [B, Hq, N]")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q) if dq is None else _given("dq", dq, q.shape, q.dtype)
+    dk = torch.empty_like(k) if dk is None else _given("dk", dk, k.shape, q.dtype)
+    dv = torch.empty_like(v) if dv is None else _given("dv", dv, v.shape, q.dtype)
     code = _dtype_code(q)
     nbytes = lib.ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, code)
     ws = _workspace(nbytes, q.device, ws)
@@ -217,10 +226,16 @@ def ks_compact_block_table(table_in, nblk_in, keep, table_out=None, nblk_out=Non
     _cuda_contig("nblk_in", nblk_in, torch.int32)
     _cuda_contig("keep", keep, torch.uint8)
     _need(tuple(keep.shape) == (B, MB) and tuple(nblk_in.shape) == (B,), "keep/nblk shape")
-    table_out = torch.empty_like(table_in) if table_out is None else table_out
-    nblk_out = torch.empty_like(nblk_in) if nblk_out is None else nblk_out
-    if pos_in is not None and pos_out is None:
-        pos_out = torch.empty_like(pos_in)
+    table_out = (torch.empty_like(table_in) if table_out is None
+                 else _given("table_out", table_out, (B, MB), torch.int32))
+    nblk_out = (torch.empty_like(nblk_in) if nblk_out is None
+                else _given("nblk_out", nblk_out, (B,), torch.int32))
+    if pos_in is not None:
+        _given("pos_in", pos_in, (B, MB), torch.int32)
+        pos_out = (torch.empty_like(pos_in) if pos_out is None
+                   else _given("pos_out", pos_out, (B, MB), torch.int32))
+    else:
+        _need(pos_out is None, "pos_out given without pos_in")
     st = lib.ks_compact_block_table(_ptr(table_in), _ptr(nblk_in), _ptr(keep), _ptr(table_out),
                                     _ptr(nblk_out), _ptr(pos_in), _ptr(pos_out), B, MB,
                                     _stream(stream))
@@ -239,10 +254,16 @@ def ks_compact_block_table_rounds(table_in, nblk_in, keeps, table_out=None, nblk
     _cuda_contig("keeps", keeps, torch.uint8)
     _need(keeps.dim() == 3 and tuple(keeps.shape[1:]) == (B, MB) and
           tuple(nblk_in.shape) == (B,), "keeps/nblk shape")
-    table_out = torch.empty_like(table_in) if table_out is None else table_out
-    nblk_out = torch.empty_like(nblk_in) if nblk_out is None else nblk_out
-    if pos_in is not None and pos_out is None:
-        pos_out = torch.empty_like(pos_in)
+    table_out = (torch.empty_like(table_in) if table_out is None
+                 else _given("table_out", table_out, (B, MB), torch.int32))
+    nblk_out = (torch.empty_like(nblk_in) if nblk_out is None
+                else _given("nblk_out", nblk_out, (B,), torch.int32))
+    if pos_in is not None:
+        _given("pos_in", pos_in, (B, MB), torch.int32)
+        pos_out = (torch.empty_like(pos_in) if pos_out is None
+                   else _given("pos_out", pos_out, (B, MB), torch.int32))
+    else:
+        _need(pos_out is None, "pos_out given without pos_in")
     st = lib.ks_compact_block_table_rounds(_ptr(table_in), _ptr(nblk_in), _ptr(keeps),
                                            keeps.shape[0], _ptr(table_out), _ptr(nblk_out),
                                            _ptr(pos_in), _ptr(pos_out), B, MB, _stream(stream))
@@ -259,8 +280,9 @@ def ks_paged_decode(q, k_pool, v_pool, table, seq_lens, scale=None, out=None, ls
     """One GQA decode step over paged caches.  Returns (out, lse)."""
     lib = load_library()
     B, Hq, D = q.shape
-    NB, Hkv, BS, _ = k_pool.shape
-    _need(BS == KS_BLOCK, "pool block size must be 16")
+    _need(k_pool.dim() == 4, "pool must be [NB, Hkv, 16, D]")
+    NB, Hkv, BS, Dp = k_pool.shape
+    _need(BS == KS_BLOCK and Dp == D, "pool must be [NB, Hkv, 16, D] with q's D")
     _cuda_contig("q", q)
     _cuda_contig("k_pool", k_pool, q.dtype)
     _cuda_contig("v_pool", v_pool, q.dtype)
@@ -269,9 +291,9 @@ def ks_paged_decode(q, k_pool, v_pool, table, seq_lens, scale=None, out=None, ls
     _need(tuple(v_pool.shape) == tuple(k_pool.shape), "v_pool shape")
     _need(table.shape[0] == B and tuple(seq_lens.shape) == (B,), "table/seq_lens shape")
     MB = table.shape[1]
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q) if out is None else _given("out", out, q.shape, q.dtype)
+    lse = (torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None
+           else _given("lse", lse, (B, Hq), torch.float32))
     nbytes = lib.ks_paged_decode_workspace(B, Hq, D, max(MB, 1))
     ws = _workspace(nbytes, q.device, ws)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
@@ -317,7 +339,7 @@ def ks_paged_decode_bs1(q, k_pool, v_pool, token_table, seq_lens, scale=None, ou
     [slots, Hkv, D], token_table [B, max_tokens].  Returns (out, lse)."""
     lib = load_library()
     B, Hq, D = q.shape
-    _need(k_pool.dim() == 3, "pool must be [slots, Hkv, D]")
+    _need(k_pool.dim() == 3 and k_pool.shape[2] == D, "pool must be [slots, Hkv, D] with q's D")
     NT, Hkv, _ = k_pool.shape
     _cuda_contig("q", q)
     _cuda_contig("k_pool", k_pool, q.dtype)
@@ -328,9 +350,9 @@ def ks_paged_decode_bs1(q, k_pool, v_pool, token_table, seq_lens, scale=None, ou
     _need(token_table.shape[0] == B and tuple(seq_lens.shape) == (B,),
           "token_table/seq_lens shape")
     MT = token_table.shape[1]
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q) if out is None else _given("out", out, q.shape, q.dtype)
+    lse = (torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None
+           else _given("lse", lse, (B, Hq), torch.float32))
     nbytes = lib.ks_paged_decode_bs1_workspace(B, Hq, D, max(MT, 1))
     ws = _workspace(nbytes, q.device, ws)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
@@ -373,7 +395,8 @@ def ks_check_eviction_record(e, bad=None, stream=None):
     _cuda_contig("e", e, torch.int32)
     _need(e.dim() == 2, "e must be [B, N]")
     B, N = e.shape
-    bad = torch.empty(B, dtype=torch.int32, device=e.device) if bad is None else bad
+    bad = (torch.empty(B, dtype=torch.int32, device=e.device) if bad is None
+           else _given("bad", bad, (B,), torch.int32))
     _check("ks_check_eviction_record",
            lib.ks_check_eviction_record(_ptr(e), B, N, _ptr(bad), _stream(stream)))
     return bad
@@ -388,7 +411,8 @@ def ks_check_block_table(table, seq_lens, num_pool_blocks, block_size=KS_BLOCK, 
     _cuda_contig("seq_lens", seq_lens, torch.int32)
     B, MB = table.shape
     _need(tuple(seq_lens.shape) == (B,), "seq_lens shape")
-    bad = torch.empty(B, dtype=torch.int32, device=table.device) if bad is None else bad
+    bad = (torch.empty(B, dtype=torch.int32, device=table.device) if bad is None
+           else _given("bad", bad, (B,), torch.int32))
     _check("ks_check_block_table",
            lib.ks_check_block_table(_ptr(table), _ptr(seq_lens), B, MB, int(num_pool_blocks),
                                     int(block_size), _ptr(bad), _stream(stream)))
@@ -402,6 +426,7 @@ def ks_paged_decode_rope(q, pos, k_pool, v_pool, table, seq_lens, base=10000.0, 
     (single-token blocks).  Returns (out, lse); q is not modified."""
     lib = load_library()
     B, Hq, D = q.shape
+    _need(k_pool.shape[-1] == D, "pool head dim must equal q's D")
     if k_pool.dim() == 4:
         NP, Hkv, BS, _ = k_pool.shape
         _need(BS == KS_BLOCK, "pool block size must be 16")
@@ -419,9 +444,9 @@ def ks_paged_decode_rope(q, pos, k_pool, v_pool, table, seq_lens, base=10000.0, 
     _need(table.shape[0] == B and tuple(seq_lens.shape) == (B,) and tuple(pos.shape) == (B,),
           "table/seq_lens/pos shape")
     ME = table.shape[1]
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q) if out is None else _given("out", out, q.shape, q.dtype)
+    lse = (torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None
+           else _given("lse", lse, (B, Hq), torch.float32))
     nbytes = (lib.ks_paged_decode_workspace(B, Hq, D, max(ME, 1)) if BS == KS_BLOCK
               else lib.ks_paged_decode_bs1_workspace(B, Hq, D, max(ME, 1)))
     ws = _workspace(nbytes, q.device, ws)
