@@ -169,6 +169,8 @@ ks_status ks_evict_attn_bwd(const void* q, const void* k, const void* v,
  *                      nblk_in are clamped to [0, max_blocks]
  * keep                 uint8 [B, max_blocks], nonzero = keep
  * pos_in, pos_out      int32 [B, max_blocks] or both NULL
+ * With max_blocks = 0 only the lengths are touched (nblk_out = 0) and the
+ * table, keep and pos pointers may be NULL.
  *
  * With single-token blocks (the SGLang setup: explainer, paragraph on padding
  * completions to whole blocks) the same call compacts token tables: entries
@@ -223,7 +225,10 @@ ks_status ks_compact_block_table_rounds(const int32_t* table_in,
  * v_pool   [num_pool_blocks, Hkv, 16, D] bf16
  * table    int32 [B, max_blocks]; entries < ceil(seq_lens[b] / 16) must be
  *          valid pool indices; an out-of-range id makes that sequence's
- *          output NaN (nothing outside the pool is read)
+ *          output NaN (nothing outside the pool is read).  With
+ *          max_blocks = 0 nothing is read: table and pools may be NULL and
+ *          every output row is 0 (lse -inf); otherwise num_pool_blocks >= 1
+ *          (KS_ERR_INVALID_ARG if not)
  * seq_lens int32 [B], 0 <= seq_lens[b] <= 16 * max_blocks; a zero-length
  *          sequence yields a zero output and lse = -inf
  * out      [B, Hq, D] bf16;  lse float [B, Hq] natural log, may be NULL

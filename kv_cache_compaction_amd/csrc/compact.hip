@@ -537,7 +537,8 @@ extern "C" ks_status ks_compact_block_table(const int32_t* table_in, const int32
   KS_REQUIRE(B >= 0 && max_blocks >= 0, "ks_compact_block_table: B=%d max_blocks=%d", B,
              max_blocks);
   if (B == 0) return KS_OK;
-  KS_REQUIRE(table_in && nblk_in && keep && table_out && nblk_out,
+  // rows of zero entries: only the lengths are read and written
+  KS_REQUIRE(nblk_in && nblk_out && (max_blocks == 0 || (table_in && keep && table_out)),
              "ks_compact_block_table: null pointer argument");
   KS_REQUIRE((pos_in == nullptr) == (pos_out == nullptr),
              "ks_compact_block_table: pos_in and pos_out must both be set or both NULL");
@@ -588,7 +589,8 @@ extern "C" ks_status ks_compact_block_table_rounds(const int32_t* table_in,
              "ks_compact_block_table_rounds: max_blocks=%d above %d", max_blocks,
              KS_MAX_ROUND_BLOCKS);
   if (B == 0) return KS_OK;
-  KS_REQUIRE(table_in && nblk_in && table_out && nblk_out && (keep || rounds == 0),
+  KS_REQUIRE(nblk_in && nblk_out &&
+                 (max_blocks == 0 || (table_in && table_out && (keep || rounds == 0))),
              "ks_compact_block_table_rounds: null pointer argument");
   KS_REQUIRE((pos_in == nullptr) == (pos_out == nullptr),
              "ks_compact_block_table_rounds: pos_in and pos_out must both be set or both NULL");

@@ -350,7 +350,12 @@ ks_status decode_impl(const char* name, const void* q, const void* k_pool, const
   const int G = Hq / Hkv;
   const int hpw = ks_heads_per_wave(G);
   if (B == 0) return KS_OK;
-  KS_REQUIRE(q && k_pool && v_pool && table && seq_lens && out, "%s: null pointer", name);
+  KS_REQUIRE(q && seq_lens && out, "%s: null pointer", name);
+  // with no table entries nothing is read through the table, so the table
+  // and the pools may be empty; otherwise an out-of-range id falls back to
+  // pool block 0, which must exist
+  KS_REQUIRE(max_entries == 0 || num_pool > 0, "%s: the pool has no blocks", name);
+  KS_REQUIRE(max_entries == 0 || (table && k_pool && v_pool), "%s: null pointer", name);
   KS_REQUIRE(ks_aligned16(q) && ks_aligned16(k_pool) && ks_aligned16(v_pool) && ks_aligned16(out),
              "%s: tensors must be 16-byte aligned", name);
   const double log2_base = qpos ? log2(static_cast<double>(base)) : 0.0;

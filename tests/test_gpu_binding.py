@@ -97,3 +97,51 @@ def test_compaction_outputs_are_checked():
     t2, n2, _ = ks.ks_compact_block_table(table, nblk, keep)
     torch.cuda.synchronize()
     assert torch.equal(t2, table) and torch.equal(n2, nblk)
+
+
+def test_empty_inputs_are_no_ops():
+    """B = 0, N = 0 and empty table rows: nothing is read, outputs are empty or
+    the documented zero rows (lse = -inf)."""
+    for B, N in ((0, 64), (2, 0)):
+        q, k, v, e = _qkv(B=B, N=N)
+        pos = torch.zeros(B, N, dtype=torch.int32, device=DEV)
+        ks.ks_rope_logical(q, k, pos)
+        o, lse = ks.ks_evict_attn_fwd(q, k, v, e)
+        dq, dk, dv = ks.ks_evict_attn_bwd(q, k, v, e, o, lse, o)
+        assert o.shape == q.shape and lse.shape == (B, 4, N) and dk.shape == k.shape
+    # compaction of zero rows and of zero-length rows
+    t0 = torch.empty(0, 7, dtype=torch.int32, device=DEV)
+    n0 = torch.empty(0, dtype=torch.int32, device=DEV)
+    t1, n1, _ = ks.ks_compact_block_table(t0, n0, torch.empty(0, 7, dtype=torch.uint8,
+                                                               device=DEV))
+    assert t1.shape == (0, 7) and n1.numel() == 0
+    tz = torch.empty(3, 0, dtype=torch.int32, device=DEV)
+    nz = torch.tensor([0, 2, 5], dtype=torch.int32, device=DEV)
+    _, nz_out, _ = ks.ks_compact_block_table(tz, nz, torch.empty(3, 0, dtype=torch.uint8,
+                                                                  device=DEV))
+    _, nz_out2, _ = ks.ks_compact_block_table_rounds(tz, nz, torch.empty(2, 3, 0,
+                                                                          dtype=torch.uint8,
+                                                                          device=DEV))
+    # decode: no sequences, and sequences whose table has no entries
+    Hq, Hkv, D = 8, 2, 128
+    pool = torch.zeros(4, Hkv, 16, D, dtype=bf, device=DEV)
+    q0 = torch.zeros(0, Hq, D, dtype=bf, device=DEV)
+    out0, lse0 = ks.ks_paged_decode(q0, pool, pool, torch.empty(0, 3, dtype=torch.int32,
+                                                                device=DEV),
+                                    torch.empty(0, dtype=torch.int32, device=DEV))
+    assert out0.shape == (0, Hq, D)
+    q = torch.ones(3, Hq, D, dtype=bf, device=DEV)
+    lens = torch.tensor([0, 5, 40], dtype=torch.int32, device=DEV)
+    empty_pool = torch.empty(0, Hkv, 16, D, dtype=bf, device=DEV)
+    out, lse = ks.ks_paged_decode(q, empty_pool, empty_pool, tz, lens)
+    pos1 = torch.full((3,), 100, dtype=torch.int32, device=DEV)
+    out_r, lse_r = ks.ks_paged_decode_rope(q, pos1, empty_pool, empty_pool, tz, lens)
+    torch.cuda.synchronize()
+    assert torch.all(nz_out == 0) and torch.all(nz_out2 == 0)
+    for o_, l_ in ((out, lse), (out_r, lse_r)):
+        assert torch.all(o_ == 0)
+        assert torch.all(torch.isinf(l_)) and torch.all(l_ < 0)
+    # entries present but no pool blocks: refused before launching
+    with pytest.raises(ks.KSError, match="no blocks"):
+        ks.ks_paged_decode(q, empty_pool, empty_pool,
+                           torch.zeros(3, 2, dtype=torch.int32, device=DEV), lens)

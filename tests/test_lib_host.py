@@ -173,3 +173,18 @@ def test_binding_signatures_match_header():
         n = 0 if params in ("", "void") else len(params.split(","))
         assert n == len(args), (name, n, len(args))
 
+
+
+def test_decode_pool_must_have_blocks_when_entries_exist(lib):
+    need = lib.ks_paged_decode_workspace(2, 32, 128, 10)
+    st, msg = _status(lib, "ks_paged_decode", *([FAKE] * 7), 2, 32, 8, 128, 10, 0, 1, 0.1,
+                      FAKE, need, None)
+    assert st == 1 and "no blocks" in msg
+    need1 = lib.ks_paged_decode_bs1_workspace(2, 32, 128, 10)
+    st, msg = _status(lib, "ks_paged_decode_bs1", *([FAKE] * 7), 2, 32, 8, 128, 10, 0, 1, 0.1,
+                      FAKE, need1, None)
+    assert st == 1 and "no blocks" in msg
+    # a null table or pool is refused while entries exist
+    st, msg = _status(lib, "ks_paged_decode", FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 32, 8,
+                      128, 10, 4, 1, 0.1, FAKE, need, None)
+    assert st == 1 and "null" in msg
