@@ -75,7 +75,7 @@ def executed_flops(e: np.ndarray, Hq: int, Hkv: int, D: int, kt: int = 64):
     the largest e of their keys, each wave skipping chunks none of its keys
     sees.  Returns (forward, dQ, dK/dV) flops."""
     G = Hq // Hkv
-    hpw = 4 if G >= 4 else G
+    hpw = 4 if G % 4 == 0 else (2 if G % 2 == 0 else 1)   # query heads per wave
     bm = 32 * (8 // hpw)
     fwd = dq = dkdv = 0
     for row in e.astype(np.int64):
@@ -401,6 +401,7 @@ def main():
     result["toy_stack"] = toy_stack_mismatch(torch)
     result["reprefill_counterfactual"] = reprefill_counterfactual(
         ks, torch, traces, q, k, v, do, stream, ms, pairs, trn)
+    result["long_mixed_64k"] = long_mixed_64k(ks, torch, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(traces, seeds, trn, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -598,6 +599,74 @@ def reprefill_counterfactual(ks, torch, traces, q, k, v, do, stream, ms, pairs, 
         "time_ratio": round(t_rp / t_ks, 4),
         "tflops_useful": round(14.0 * D * pairs_rp * Hq / (t_rp * 1e-3) / 1e12, 2),
     }
+
+
+def long_mixed_64k(ks, torch, stream, reps=5):
+    """Masked fwd+bwd of the long mixed workload: 8 traces of 65,536 tokens
+    compacted by sliding window, prompt+recent and summary in turn, 64 q /
+    8 kv heads, D = 128.  Median over reps of each pass, timed with HIP
+    events on the library's stream; useful TFLOP/s with the step's
+    convention (RoPE applied once beforehand, not timed)."""
+    from workloads import LONG_MIXED_64K, config_trace_batch, normal_tensor, stacked_e
+
+    cfg = LONG_MIXED_64K
+    traces, seeds = config_trace_batch(cfg)
+    e_np = stacked_e(traces)
+    B, N, Hq, Hkv, D = cfg.batch, cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+    dev, bf = "cuda", torch.bfloat16
+    q = normal_tensor((B, N, Hq, D), seeds["q"], cfg.value_scale, bf, dev)
+    k = normal_tensor((B, N, Hkv, D), seeds["k"], cfg.value_scale, bf, dev)
+    v = normal_tensor((B, N, Hkv, D), seeds["v"], cfg.value_scale, bf, dev)
+    do = normal_tensor((B, N, Hq, D), seeds["do"], cfg.value_scale, bf, dev)
+    e = torch.from_numpy(e_np).to(dev)
+    pos = torch.arange(N, dtype=torch.int32, device=dev)[None].repeat(B, 1).contiguous()
+    ks.ks_rope_logical(q, k, pos, stream=stream)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsf = torch.empty(ks.ks_evict_attn_fwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+                      dtype=torch.uint8, device=dev)
+    wsb = torch.empty(ks.ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+                      dtype=torch.uint8, device=dev)
+    fwd = lambda: ks.ks_evict_attn_fwd(q, k, v, e, out=o, lse=lse, ws=wsf, stream=stream)
+    bwd = lambda: ks.ks_evict_attn_bwd(q, k, v, e, o, lse, do, dq=dq, dk=dk, dv=dv, ws=wsb,
+                                       stream=stream)
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    t_f, t_b = [], []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        fwd()
+        ev[1].record(stream)
+        bwd()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_f.append(ev[0].elapsed_time(ev[1]))
+        t_b.append(ev[1].elapsed_time(ev[2]))
+    mf, mb = float(np.median(t_f)), float(np.median(t_b))
+    pairs = live_pairs(e_np)
+    useful_f = 4.0 * D * pairs * Hq
+    useful_b = 10.0 * D * pairs * Hq
+    ex_f, ex_q, ex_kv = executed_flops(e_np, Hq, Hkv, D)
+    out = {
+        "workload": "8 x 65536-token traces (sliding window, prompt+recent, summary "
+                    "o=2048 s=1024; P=512, B=16384), 64 q / 8 kv heads, D=128, fwd+bwd",
+        "events_per_trace": [len(tr.events) for tr in traces],
+        "live_pairs_per_head": int(pairs),
+        "ms_fwd": round(mf, 3),
+        "ms_bwd": round(mb, 3),
+        "useful_tflop": round((useful_f + useful_b) / 1e12, 2),
+        "tflops_useful": round((useful_f + useful_b) / ((mf + mb) * 1e-3) / 1e12, 2),
+        "frac_of_bf16_peak": round((useful_f + useful_b) / ((mf + mb) * 1e-3) / 2516.6e12, 4),
+        "fwd_tflops_useful": round(useful_f / (mf * 1e-3) / 1e12, 2),
+        "bwd_tflops_useful": round(useful_b / (mb * 1e-3) / 1e12, 2),
+        "executed_over_useful": round((ex_f + ex_q + ex_kv) / (useful_f + useful_b), 4),
+    }
+    del q, k, v, do, o, dq, dk, dv, wsf, wsb
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(traces, seeds, cfg, budget_s):
