@@ -8,7 +8,8 @@ import torch
 import kv_cache_compaction_amd as ks
 import oracle as O
 from parity_util import announce, f64, gate
-from workloads import SUMMARY_32K, config_trace_batch, normal_tensor, stacked_e
+from workloads import (SUMMARY_32K, build_trace, check_trace, config_trace_batch,
+                       normal_tensor, stacked_e)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -88,3 +89,47 @@ def test_summary_32k_sampled():
         return [np.arange(tr.N - 64, tr.N),                      # queries [j, N)
                 np.arange(t1 - 1536 - 64, t1 - 1536)]            # evicted at t1
     run_training_config(SUMMARY_32K, b=1, hkv=3, key_blocks=key_blocks)
+
+
+def test_trace_past_one_live_window():
+    """A 132,096-token trace: the forward and dQ kernels list live key tiles
+    in windows of 2,048 tiles (131,072 tokens), so query tiles past that
+    point gather theirs from two windows (the pinned prompt and older recent
+    turns in the first, the newest turns in the second).  Sampled rows there
+    and key blocks on both sides of the boundary against the oracle."""
+    N, Hq, Hkv, D = 132096, 8, 2, 128
+    G = Hq // Hkv
+    tr = build_trace(np.random.default_rng(77), N, 512, 8192, "recent")
+    check_trace(tr)
+    e = tr.e[None].astype(np.int32)
+    bf = torch.bfloat16
+    q = normal_tensor((1, N, Hq, D), 7701, 0.5, bf, DEV)
+    k = normal_tensor((1, N, Hkv, D), 7702, 0.5, bf, DEV)
+    v = normal_tensor((1, N, Hkv, D), 7703, 0.5, bf, DEV)
+    do = normal_tensor((1, N, Hq, D), 7704, 0.5, bf, DEV)
+    eg = torch.from_numpy(e).to(DEV)
+    o, lse = ks.ks_evict_attn_fwd(q, k, v, eg)
+    dq, dk, dv = ks.ks_evict_attn_bwd(q, k, v, eg, o, lse, do)
+    torch.cuda.synchronize()
+    hkv = 1
+    heads = slice(hkv * G, (hkv + 1) * G)
+    qh, kh, vh, doh = (f64(q[:, :, heads]), f64(k[:, :, hkv:hkv + 1]),
+                       f64(v[:, :, hkv:hkv + 1]), f64(do[:, :, heads]))
+    w = 2048 * 64
+    rng = np.random.default_rng(78)
+    rows = {w - 1, w, w + 1, w + 63, w + 64, N - 65, N - 64, N - 2, N - 1}
+    rows.update(t for t in tr.events if t < N)
+    rows.update(int(x) for x in rng.integers(w, N, 12))
+    rows.update(int(x) for x in rng.integers(0, w, 6))
+    rows = np.array(sorted(r for r in rows if 0 <= r < N))
+    e64 = e.astype(np.int64)
+    for hh in range(G):
+        ro, rl = O.attn_fwd_rows(qh, kh, vh, e64, 0, hh, rows)
+        gate(o[0, rows, hkv * G + hh], ro, "bf16", f"O rows h{hh}")
+        gate(lse[0, hkv * G + hh, rows], rl, "bf16", f"LSE rows h{hh}")
+        rdq = O.attn_bwd_rows(qh, kh, vh, e64, doh, 0, hh, rows)
+        gate(dq[0, rows, hkv * G + hh], rdq, "bf16grad", f"dQ rows h{hh}")
+    for keys in (np.arange(N - 64, N), np.arange(w - 32, w + 32)):
+        rdk, rdv = O.attn_bwd_keys(qh, kh, vh, e64, doh, 0, 0, keys)
+        gate(dk[0, keys, hkv], rdk, "bf16grad", f"dK keys {keys[0]}..")
+        gate(dv[0, keys, hkv], rdv, "bf16grad", f"dV keys {keys[0]}..")
