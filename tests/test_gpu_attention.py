@@ -61,9 +61,10 @@ def test_tiny512_f32_rope_then_forward():
     gate(lse, rl, "f32", "LSE")
 
 
-@pytest.mark.parametrize("N,G,seed", [(1, 1, 1), (63, 1, 2), (200, 2, 3), (333, 4, 4)])
-def test_f32_forward_random_masks(N, G, seed):
-    B, Hkv, D = 2, 2, 64
+@pytest.mark.parametrize("N,G,D,seed", [(1, 1, 64, 1), (63, 1, 64, 2), (200, 2, 64, 3),
+                                        (333, 4, 64, 4), (150, 3, 128, 5), (97, 1, 128, 6)])
+def test_f32_forward_random_masks(N, G, D, seed):
+    B, Hkv = 2, 2
     rng = np.random.default_rng(seed)
     e = _random_e(rng, B, N)
     q, k, v, _ = _inputs(B, N, Hkv * G, Hkv, D, 100 + seed, torch.float32, 1.0)
@@ -125,7 +126,9 @@ def test_train4k_negative_controls(train4k):
     (1, 4, 1, 128, 1), (65, 4, 4, 128, 2), (300, 8, 2, 128, 3), (517, 8, 1, 128, 4),
     (700, 2, 1, 128, 5), (450, 4, 2, 64, 6), (129, 16, 2, 128, 7),
     # group sizes 3 and 6: one and two query heads per wave
-    (150, 6, 2, 128, 8), (140, 12, 2, 128, 9), (90, 3, 1, 64, 10), (77, 12, 2, 64, 11)])
+    (150, 6, 2, 128, 8), (140, 12, 2, 128, 9), (90, 3, 1, 64, 10), (77, 12, 2, 64, 11),
+    # D = 64 with four query heads per wave
+    (180, 8, 2, 64, 12), (65, 8, 1, 64, 13)])
 def test_bf16_forward_random_masks(N, Hq, Hkv, D, seed):
     B = 2
     rng = np.random.default_rng(seed)

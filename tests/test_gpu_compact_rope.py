@@ -157,7 +157,7 @@ def test_rope_f32_tiny512_positions():
     np.testing.assert_allclose(f64(kg), O.rope(f64(k), pos), atol=1e-5, rtol=0)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 96, 128, 256])
 def test_rope_bf16_large_logical_positions(D):
     B, N, Hq, Hkv = 3, 37, 8, 2
     q = normal_tensor((B, N, Hq, D), 21, 0.5, torch.bfloat16)
