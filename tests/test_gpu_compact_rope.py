@@ -145,8 +145,9 @@ def test_compact_rejects_aliasing_on_device():
         ks.ks_compact_block_table(t, n, k, t, n)
 
 
-def test_rope_f32_tiny512_positions():
-    B, N, Hq, Hkv, D = 1, 512, 1, 1, 64
+@pytest.mark.parametrize("D", [64, 48, 256])
+def test_rope_f32_tiny512_positions(D):
+    B, N, Hq, Hkv = 1, 512, 1, 1
     q = normal_tensor((B, N, Hq, D), 11)
     k = normal_tensor((B, N, Hkv, D), 12)
     pos = np.arange(N, dtype=np.int32)[None]
