@@ -370,7 +370,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   lin = (lin & 7) * (total_wg >> 3) + (lin >> 3);
   const int ngrp = Hq / HPW;
   if (lin >= B * ngrp * nqt) return;
-  const int qt = lin % nqt;
+  // query tiles in descending order: the first tiles of a trace see only a
+  // short causal prefix, so they are the short workgroups left for the end
+  const int qt = nqt - 1 - lin % nqt;
   const int grp = (lin / nqt) % ngrp;
   const int b = lin / (nqt * ngrp);
   const int G = Hq / Hkv;
