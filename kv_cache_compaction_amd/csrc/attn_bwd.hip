@@ -31,46 +31,12 @@ constexpr int KW = 256;        // keys per dK/dV workgroup (8 waves x 32)
 constexpr int KT = kKeyTile;   // keys per dQ tile
 
 // ---------------------------------------------------------------------------
-// D_i = sum_d dO_id O_id (fp32) and LSE in log2 units, kept as one record
-// per 32-row query chunk of every (batch, head): rec[b][h][c][64] holds the
-// LSE of rows 32 c .. 32 c + 31, then their D_i (256 bytes, one DMA unit).
-// Rows past N (up to Npad = N rounded up to BQ) hold 0.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_pre_kernel(
-    const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ rec, long long rows, int N, int Npad, int Hq) {
-  // 16 threads per (b, i, h) row of D = 128 values; rows past B*N*Hq are padding
-  const long long r = static_cast<long long>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int c = threadIdx.x & 15;
-  float acc = 0.f;
-  if (r < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + r * D + c * 8);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(dout + r * D + c * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc += lo_bf16(a[i]) * lo_bf16(g[i]) + hi_bf16(a[i]) * hi_bf16(g[i]);
-  }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (c != 0) return;
-  if (r < rows) {
-    // r = (b * N + i) * Hq + h  ->  [(b * Hq + h) * Npad + i]
-    const long long h = r % Hq;
-    const long long bi = r / Hq;
-    const long long b = bi / N, i = bi % N;
-    const long long bh = b * Hq + h;
-    float* r0 = rec + (bh * (Npad / BQ) + i / BQ) * (2 * BQ) + i % BQ;
-    r0[0] = lse[bh * N + i] * KS_LOG2E;
-    r0[BQ] = acc;
-  } else if (Npad > N) {
-    const long long pr = r - rows;  // padding entry pr of (Npad - N) per (b, h)
-    const long long bh = pr / (Npad - N), i = N + pr % (Npad - N);
-    float* r0 = rec + (bh * (Npad / BQ) + i / BQ) * (2 * BQ) + i % BQ;
-    r0[0] = 0.f;
-    r0[BQ] = 0.f;
-  }
-}
-
+// Softmax records: rec[b][h][c][64] holds, for the 32-row query chunk c of
+// every (batch, head), the LSE of rows 32 c .. 32 c + 31 in log2 units, then
+// their D_i = sum_d dO_id O_id (fp32): 256 bytes, one DMA unit.  Rows past N
+// (up to Npad = N rounded up to BQ) hold 0.  The dQ kernel forms them (it
+// holds each query row's dO in registers anyway) and dK/dV, launched after
+// it, stages them with its query chunks.
 // ---------------------------------------------------------------------------
 // dK, dV.  K stays in registers as the B operand of S = Q K^T; V of the 256
 // keys stays in LDS for the whole walk (B operand of dP = dO V^T).  Query
@@ -354,9 +320,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <int HPW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const TileSummary ts, const float* __restrict__ rec,
-    const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq, int B, int N, int Npad, int Hq,
-    int Hkv, int ntiles, int nqt, int total_wg, float scale) {
+    const TileSummary ts, float* __restrict__ rec, const bf16_t* __restrict__ o,
+    const float* __restrict__ lse, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
+    int B, int N, int Npad, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale) {
   constexpr int RS = 8 / HPW;
   constexpr int BM = 32 * RS;
   __shared__ __attribute__((aligned(16))) bf16_t S0[kKvElems];
@@ -397,24 +363,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   KvStager stg;
   stg.init(w, lane);
 
+  // Q and dO rows in registers; D_i = sum_d dO_id O_id of this lane's row
+  // from the two half rows of the lane pair (lq, lq + 32), and the row's LSE
+  // in log2 units; the row's record (LSE, D_i) is also written for dK/dV,
+  // which runs after this kernel (rows N .. Npad - 1 get zeros)
   bf16x8 qf[NSTEP], gf[NSTEP];
   float l2, dii;
   {
     const size_t off = (static_cast<size_t>(b) * N + (qi < N ? qi : 0)) * tokq +
                        static_cast<size_t>(hq) * D + lh * 8;
+    float acc = 0.f;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       u32x4 a = *reinterpret_cast<const u32x4*>(q + off + s * 16);
       u32x4 c = *reinterpret_cast<const u32x4*>(dout + off + s * 16);
-      if (qi >= N) a = c = u32x4{0u, 0u, 0u, 0u};
+      u32x4 ov = *reinterpret_cast<const u32x4*>(o + off + s * 16);
+      if (qi >= N) a = c = ov = u32x4{0u, 0u, 0u, 0u};
       qf[s] = __builtin_bit_cast(bf16x8, a);
       gf[s] = __builtin_bit_cast(bf16x8, c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc += lo_bf16(c[i]) * lo_bf16(ov[i]) + hi_bf16(c[i]) * hi_bf16(ov[i]);
     }
-    const int qr = qi < N ? qi : 0;
-    const float* r0 =
-        rec + ((static_cast<size_t>(b) * Hq + hq) * (Npad / BQ) + qr / BQ) * (2 * BQ) + qr % BQ;
-    l2 = qi < N ? r0[0] : INFINITY;
-    dii = qi < N ? r0[BQ] : 0.f;
+    acc += __shfl_xor(acc, 32);
+    const float lv = qi < N ? lse[(static_cast<size_t>(b) * Hq + hq) * N + qi] * KS_LOG2E : 0.f;
+    l2 = qi < N ? lv : INFINITY;
+    dii = qi < N ? acc : 0.f;
+    if (lh == 0 && qi < Npad) {
+      float* r0 =
+          rec + ((static_cast<size_t>(b) * Hq + hq) * (Npad / BQ) + qi / BQ) * (2 * BQ) + qi % BQ;
+      r0[0] = qi < N ? lv : 0.f;
+      r0[BQ] = dii;
+    }
   }
   wait_vm<0>();  // Q, dO in registers before the DMA stream starts
   f32x16 dqa[NDB];
@@ -585,35 +565,29 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   const bf16_t* vv = static_cast<const bf16_t*>(v);
   const bf16_t* gg = static_cast<const bf16_t*>(dout);
 
-  const long long rows = static_cast<long long>(B) * N * Hq;
-  const long long prows = rows + static_cast<long long>(B) * Hq * (Npad - N);
-  KS_REQUIRE((prows + 15) / 16 < (1LL << 31), "ks_evict_attn_bwd: too many rows");
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3(static_cast<unsigned>((prows + 15) / 16)), dim3(256),
-                     0, s, static_cast<const bf16_t*>(o), gg, lse, rec, rows, N, Npad, Hq);
-  st = ks_check_launch("ks_evict_attn_bwd(pre)");
-  if (st != KS_OK) return st;
-
-  const int nkt = (N + KW - 1) / KW;
-  const long long nkv = static_cast<long long>(B) * Hkv * nkt;
-  KS_REQUIRE(nkv < (1LL << 31), "ks_evict_attn_bwd: grid too large");
-  hipLaunchKernelGGL(dkdv_kernel, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq, kk,
-                     vv, e, emin, emax, rec, gg, static_cast<bf16_t*>(dk),
-                     static_cast<bf16_t*>(dv), B, N, Npad, Hq, Hkv, ntiles, scale);
-  st = ks_check_launch("ks_evict_attn_bwd(dkdv)");
-  if (st != KS_OK) return st;
-
+  // dQ first: it forms D_i and the LSE records of every row, which dK/dV reads
   const int rs = 8 / hpw;
   const int nqt = (N + 32 * rs - 1) / (32 * rs);
   const long long real_q = static_cast<long long>(B) * (Hq / hpw) * nqt;
   const long long total_q = (real_q + 7) / 8 * 8;
   KS_REQUIRE(total_q < (1LL << 31), "ks_evict_attn_bwd: grid too large");
+  const int nkt = (N + KW - 1) / KW;
+  const long long nkv = static_cast<long long>(B) * Hkv * nkt;
+  KS_REQUIRE(nkv < (1LL << 31), "ks_evict_attn_bwd: grid too large");
+  const bf16_t* oo = static_cast<const bf16_t*>(o);
 #define KS_DQ_LAUNCH(HPW_)                                                                   \
   hipLaunchKernelGGL((dq_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(512), \
-                     0, s, qq, kk, vv, ts, rec, gg, static_cast<bf16_t*>(dq), B, N, Npad,        \
-                     Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
+                     0, s, qq, kk, vv, ts, rec, oo, lse, gg, static_cast<bf16_t*>(dq), B, N, \
+                     Npad, Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
   if (hpw == 4) KS_DQ_LAUNCH(4);
   else if (hpw == 2) KS_DQ_LAUNCH(2);
   else KS_DQ_LAUNCH(1);
 #undef KS_DQ_LAUNCH
-  return ks_check_launch("ks_evict_attn_bwd(dq)");
+  st = ks_check_launch("ks_evict_attn_bwd(dq)");
+  if (st != KS_OK) return st;
+
+  hipLaunchKernelGGL(dkdv_kernel, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq, kk,
+                     vv, e, emin, emax, rec, gg, static_cast<bf16_t*>(dk),
+                     static_cast<bf16_t*>(dv), B, N, Npad, Hq, Hkv, ntiles, scale);
+  return ks_check_launch("ks_evict_attn_bwd(dkdv)");
 }
