@@ -105,6 +105,124 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
   if (tid == 0) nout[b] = base;
 }
 
+// Rows whose length is a multiple of 16 entries, on 16-byte aligned tables:
+// one workgroup per row of up to 4096 entries, one pass, 256 threads x 16
+// consecutive entries read with four 16-byte loads (and the keep flags with
+// one).  Kept entries are placed at their ranks in LDS and the row (kept
+// entries, then -1) is written out with 16-byte stores, each store
+// instruction covering 1 KB of the row.  Other rows take compact_kernel.
+constexpr int kCThreads = 256;
+constexpr int kCPer = 16;
+constexpr int kCWaves = kCThreads / 64;
+constexpr int kCRow = kCThreads * kCPer;   // 4096 entries
+
+__global__ __launch_bounds__(kCThreads) void compact_vec_kernel(
+    const int32_t* __restrict__ tin, const int32_t* __restrict__ nin,
+    const uint8_t* __restrict__ keep, int32_t* __restrict__ tout,
+    int32_t* __restrict__ nout, const int32_t* __restrict__ pin,
+    int32_t* __restrict__ pout, int MB) {
+  __shared__ int wsum[kCWaves];
+  __shared__ __attribute__((aligned(16))) int stage[kCRow];
+  const int b = blockIdx.x;
+  const size_t row = static_cast<size_t>(b) * MB;
+  const int tid = threadIdx.x, w = tid >> 6;
+  if (MB == 0) {
+    if (tid == 0) nout[b] = 0;
+    return;
+  }
+  // the loads do not depend on the length: they go out with its load
+  const int k0 = tid * kCPer;
+  int vals[kCPer];
+  uint32_t kw[kCPer / 4];  // keep flags, one byte each, four per word
+  const bool vec = k0 + kCPer <= MB;  // threads past the row end read nothing
+  if (vec) {
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(keep + row + k0);
+    kw[0] = kv[0];
+    kw[1] = kv[1];
+    kw[2] = kv[2];
+    kw[3] = kv[3];
+#pragma unroll
+    for (int qd = 0; qd < kCPer / 4; ++qd) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(tin + row + k0 + 4 * qd);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) vals[4 * qd + c] = static_cast<int>(t[c]);
+    }
+  } else {
+#pragma unroll
+    for (int qd = 0; qd < kCPer / 4; ++qd) kw[qd] = 0u;
+#pragma unroll
+    for (int u = 0; u < kCPer; ++u) vals[u] = 0;
+  }
+  int n = nin[b];
+  n = n < 0 ? 0 : (n > MB ? MB : n);
+  uint32_t fl = 0;
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < kCPer; ++u) {
+    const bool ok = k0 + u < n && ((kw[u >> 2] >> (8 * (u & 3))) & 0xffu) != 0;
+    fl |= static_cast<uint32_t>(ok) << u;
+    cnt += ok;
+  }
+  // exclusive prefix of `cnt` over the workgroup: within-wave via ballots of
+  // each bit of cnt (cnt <= 16 needs 5 bits), then across waves through LDS
+  int pre = 0;
+  int tot_w = 0;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) {
+    const uint64_t m = __ballot((cnt >> bit) & 1);
+    pre += lane_rank(m) << bit;
+    tot_w += __popcll(m) << bit;
+  }
+  if ((tid & 63) == 0) wsum[w] = tot_w;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kCWaves; ++i) {
+    const int s = wsum[i];
+    off += (i < w) ? s : 0;
+    tot += s;
+  }
+  // the kept entries at their ranks, then the whole row written out in order
+  auto place_and_write = [&](const int* v, int32_t* dst_row) {
+    int d = off + pre;
+#pragma unroll
+    for (int u = 0; u < kCPer; ++u)
+      if ((fl >> u) & 1u) stage[d++] = v[u];
+    __syncthreads();
+    // thread t writes entries 4 t + 1024 q .. + 3
+#pragma unroll
+    for (int qd = 0; qd < kCPer / 4; ++qd) {
+      const int x = 4 * tid + kCThreads * 4 * qd;
+      if (x < MB) {
+        u32x4 o;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          o[c] = static_cast<uint32_t>(x + c < tot ? stage[x + c] : -1);
+        *reinterpret_cast<u32x4*>(dst_row + x) = o;
+      }
+    }
+  };
+  place_and_write(vals, tout + row);
+  if (pout) {
+    // positions follow the same selection, through the same staging buffer
+    __syncthreads();
+    int pv[kCPer];
+    if (vec) {
+#pragma unroll
+      for (int qd = 0; qd < kCPer / 4; ++qd) {
+        const u32x4 p = *reinterpret_cast<const u32x4*>(pin + row + k0 + 4 * qd);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pv[4 * qd + c] = static_cast<int>(p[c]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kCPer; ++u) pv[u] = 0;
+    }
+    place_and_write(pv, pout + row);
+  }
+  if (tid == 0) nout[b] = tot;
+}
+
 // ---------------------------------------------------------------------------
 // Several events in one launch.  Thread t owns positions 4t .. 4t + 3 of the
 // current table of its sequence, so the keep flags of every event sit at
@@ -557,8 +675,16 @@ extern "C" ks_status ks_compact_block_table(const int32_t* table_in, const int32
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_blocks <= kRoundBlocks) {
-    hipLaunchKernelGGL(compact_kernel, dim3(B), dim3(kThreads), 0, s, table_in, nblk_in, keep,
-                       table_out, nblk_out, pos_in, pos_out, max_blocks);
+    // whole rows by 16-byte loads and stores when every row starts aligned
+    const bool vec = max_blocks % kCPer == 0 && ks_aligned16(table_in) && ks_aligned16(keep) &&
+                     ks_aligned16(table_out) && (!pos_in || ks_aligned16(pos_in)) &&
+                     (!pos_out || ks_aligned16(pos_out));
+    if (vec)
+      hipLaunchKernelGGL(compact_vec_kernel, dim3(B), dim3(kCThreads), 0, s, table_in, nblk_in,
+                         keep, table_out, nblk_out, pos_in, pos_out, max_blocks);
+    else
+      hipLaunchKernelGGL(compact_kernel, dim3(B), dim3(kThreads), 0, s, table_in, nblk_in, keep,
+                         table_out, nblk_out, pos_in, pos_out, max_blocks);
     return ks_check_launch("ks_compact_block_table");
   }
   KS_REQUIRE(B < 65536, "ks_compact_block_table: B=%d too large for rows above %d entries", B,

@@ -116,25 +116,38 @@ def test_compact_rounds_random_and_edges(B, MB, R, seed):
     np.testing.assert_array_equal(po.cpu().numpy(), rp)
 
 
-@pytest.mark.parametrize("B,MB,seed", [(1, 1, 0), (3, 5, 1), (7, 4096, 2), (2, 10000, 3),
-                                       (5, 4097, 4)])
-def test_compact_random_and_edges(B, MB, seed):
+# widths that are a multiple of 16 (64, 2048, 4096) take the whole-row
+# vector kernel, the others the entry-by-entry one; rows past 4096 entries
+# are split over several workgroups
+@pytest.mark.parametrize("B,MB,seed,with_pos", [
+    (1, 1, 0, False), (3, 5, 1, False), (7, 4096, 2, False), (2, 10000, 3, False),
+    (5, 4097, 4, False), (6, 64, 5, True), (5, 2048, 6, True), (4, 4096, 7, True),
+    (6, 4088, 8, True)])
+def test_compact_random_and_edges(B, MB, seed, with_pos):
     rng = np.random.default_rng(seed)
     table = rng.integers(0, 2**31 - 1, size=(B, MB)).astype(np.int32)
+    pos = rng.integers(0, 2**31 - 1, size=(B, MB)).astype(np.int32)
     nblk = rng.integers(0, MB + 1, size=B).astype(np.int32)
     nblk[0] = MB
     if B > 1:
         nblk[1] = 0
+    if B > 4:
+        nblk[4] = MB + 7     # clamped to MB
     keep = (rng.random((B, MB)) < 0.7).astype(np.uint8)
     if B > 2:
         keep[2] = 1
     if B > 3:
         keep[3] = 0
-    out, n, _ = ks.ks_compact_block_table(_gpu(table), _gpu(nblk), _gpu(keep))
-    ref, rn = O.compact_block_table(table, nblk, keep)
+    out, n, po = ks.ks_compact_block_table(_gpu(table), _gpu(nblk), _gpu(keep),
+                                           pos_in=_gpu(pos) if with_pos else None)
+    nb = np.clip(nblk, 0, MB)
+    ref, rn = O.compact_block_table(table, nb, keep)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), ref)
     np.testing.assert_array_equal(n.cpu().numpy(), rn)
+    if with_pos:
+        rp, _ = O.compact_block_table(pos, nb, keep)
+        np.testing.assert_array_equal(po.cpu().numpy(), rp)
 
 
 def test_compact_rejects_aliasing_on_device():
