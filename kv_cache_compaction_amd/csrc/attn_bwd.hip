@@ -5,13 +5,16 @@
 //   P = exp(S - LSE), dV = P^T dO, dP = dO V^T, D_i = rowsum(dO o O),
 //   dS = P o (dP - D_i), dQ = scale dS K, dK = scale dS^T Q.
 //
-// Deterministic two-kernel split (no atomics, no fp32 dQ workspace):
+// Deterministic two-kernel split (no atomics, no fp32 dQ workspace), in
+// launch order:
+//   dq_kernel    query-tile outer, laid out like the forward:
+//                S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T; its prologue
+//                forms D_i of each query row and writes the (LSE, D_i)
+//                records the second kernel stages.
 //   dkdv_kernel  key-tile outer: a workgroup owns 256 keys of one kv head and
 //                walks every query head of the group over the query rows
 //                that can see them, [j0, max e_j), in 32-row chunks:
 //                S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
-//   dq_kernel    query-tile outer, laid out like the forward:
-//                S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
 // The pair executes 14*D flops per live (query, key, head) triple against
 // the 10*D of a fused kernel, in exchange for no atomic traffic at all.
 // Both run 8 waves per workgroup (2 per SIMD) on tiles staged in natural
