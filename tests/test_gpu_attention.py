@@ -291,3 +291,50 @@ def test_f32_broken_records():
     for b in range(B):
         assert np.all(np.isneginf(lg[b][:, empty[b]]))
         gate(lg[b][:, ~empty[b]], rl[b][:, ~empty[b]], "f32", "LSE")
+
+
+def test_training_pass_replays_from_a_graph():
+    """RoPE, masked forward and backward are capture-safe (the library records
+    no memsets and allocates nothing): a captured graph, which first restores
+    the unrotated q and k, replays to the eager results every time, with
+    eager work on the same tensors in between."""
+    rng = np.random.default_rng(61)
+    B, N, Hq, Hkv, D = 2, 700, 8, 2, 128
+    e = _random_e(rng, B, N)
+    q0, k0, v, do = (t.to(DEV) for t in _inputs(B, N, Hq, Hkv, D, 610, torch.bfloat16))
+    eg = _e_gpu(e)
+    pos = torch.arange(N, dtype=torch.int32, device=DEV)[None].repeat(B, 1).contiguous()
+    q, k = torch.empty_like(q0), torch.empty_like(k0)
+    o = torch.empty_like(q0)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=DEV)
+    dq, dk, dv = torch.empty_like(q0), torch.empty_like(k0), torch.empty_like(v)
+    wsf = torch.empty(ks.ks_evict_attn_fwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+                      dtype=torch.uint8, device=DEV)
+    wsb = torch.empty(ks.ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+                      dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+
+    def step():
+        q.copy_(q0)
+        k.copy_(k0)
+        ks.ks_rope_logical(q, k, pos, stream=s)
+        ks.ks_evict_attn_fwd(q, k, v, eg, out=o, lse=lse, ws=wsf, stream=s)
+        ks.ks_evict_attn_bwd(q, k, v, eg, o, lse, do, dq=dq, dk=dk, dv=dv, ws=wsb, stream=s)
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in (q, o, lse, dq, dk, dv)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(4):
+            for t in (q, k, o, dq, dk, dv):
+                t.fill_(7)
+            lse.zero_()
+            wsb.fill_(255)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for got, want in zip((q, o, lse, dq, dk, dv), ref):
+                assert torch.equal(got, want)
