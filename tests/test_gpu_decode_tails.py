@@ -1,0 +1,88 @@
+"""GPU parity of paged decode on split tails: sequences whose last split has
+an odd number of 16-token groups and ends in a full group (the final group
+is processed after the paired main loop, with no masking), beside even and
+partial tails, for every heads-per-wave variant (1, 2 and 4 heads per wave)
+and both block sizes.  Checked against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compaction_amd as ks
+import oracle as O
+from parity_util import announce, f64, gate
+from workloads import normal_tensor
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+D = 128
+# 16-token groups per sequence: odd tails of a 48-group split (1, 3, 47 mod
+# 48), even tails, and one exactly full split
+GROUPS = [1, 3, 47, 49, 51, 95, 97, 2, 50, 48]
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    announce(request.node.nodeid)
+
+
+def _gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _lengths(partial):
+    g = np.array(GROUPS, np.int64)
+    # full final group, or 5 tokens short of it
+    return (16 * g - (5 if partial else 0)).astype(np.int32)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4])          # 1, 2, 1, 4 heads per wave
+@pytest.mark.parametrize("partial", [False, True])
+def test_decode_split_tails(G, partial):
+    Hkv = 2
+    Hq = G * Hkv
+    lens = _lengths(partial)
+    B = len(lens)
+    nblk = (lens + 15) // 16
+    MB = int(nblk.max())
+    NB = int(nblk.sum()) + 7
+    rng = np.random.default_rng(900 + 10 * G + partial)
+    perm = rng.permutation(NB).astype(np.int32)
+    table = np.full((B, MB), -1, np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+    seed = 9100 + 10 * G + partial
+    kp = normal_tensor((NB, Hkv, 16, D), seed, 0.5, torch.bfloat16, DEV)
+    vp = normal_tensor((NB, Hkv, 16, D), seed + 1, 0.5, torch.bfloat16, DEV)
+    q = normal_tensor((B, Hq, D), seed + 2, 0.5, torch.bfloat16, DEV)
+    out, lse = ks.ks_paged_decode(q, kp, vp, _gpu(table), _gpu(lens))
+    torch.cuda.synchronize()
+    ro, rl = O.paged_decode(f64(q), f64(kp), f64(vp), table, lens)
+    gate(out, ro, "bf16", f"decode tails G{G} partial={partial}")
+    gate(lse, rl, "bf16", f"decode tails lse G{G} partial={partial}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4])
+def test_decode_bs1_split_tails(G):
+    Hkv = 2
+    Hq = G * Hkv
+    lens = _lengths(False)
+    B = len(lens)
+    NT = int(lens.sum()) + 33
+    rng = np.random.default_rng(950 + G)
+    perm = rng.permutation(NT).astype(np.int32)
+    table = np.full((B, int(lens.max())), -1, np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :lens[b]] = perm[off:off + lens[b]]
+        off += lens[b]
+    seed = 9500 + 10 * G
+    kp = normal_tensor((NT, Hkv, D), seed, 0.5, torch.bfloat16, DEV)
+    vp = normal_tensor((NT, Hkv, D), seed + 1, 0.5, torch.bfloat16, DEV)
+    q = normal_tensor((B, Hq, D), seed + 2, 0.5, torch.bfloat16, DEV)
+    out, lse = ks.ks_paged_decode_bs1(q, kp, vp, _gpu(table), _gpu(lens))
+    torch.cuda.synchronize()
+    ro, rl = O.paged_decode(f64(q), f64(kp)[:, :, None], f64(vp)[:, :, None], table, lens)
+    gate(out, ro, "bf16", f"decode bs1 tails G{G}")
+    gate(lse, rl, "bf16", f"decode bs1 tails lse G{G}")
