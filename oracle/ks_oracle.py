@@ -139,27 +139,35 @@ def attn_fwd(q, k, v, e, scale=None, row_chunk=512):
 
 
 def _bwd_rows_core(q, k, v, e, do, b, h, rows, scale):
-    """P, dS and the row-local pieces for query rows ``rows`` of head h."""
+    """P, dS and the row-local pieces for query rows ``rows`` of head h.
+
+    The sums run over the live set: a key column that no row of ``rows``
+    may attend (M_ij = 0 in every row) has P = dS = 0 there, so only the
+    columns ``cols`` live for at least one row are formed; the mask is still
+    applied element by element inside them.
+    """
     Hq, Hkv, D = q.shape[2], k.shape[2], q.shape[3]
     kv = h // (Hq // Hkv)
     sc = _scale(D, scale)
     rows = np.asarray(rows, dtype=np.int64)
     n_keys = int(rows.max()) + 1
+    M = eviction_mask(e[b], rows, n_keys)
+    cols = np.flatnonzero(M.any(axis=0))
+    M = M[:, cols]
     qq = np.asarray(q[b, rows, h], dtype=np.float64)
-    kk = np.asarray(k[b, :n_keys, kv], dtype=np.float64)
-    vv = np.asarray(v[b, :n_keys, kv], dtype=np.float64)
+    kk = np.asarray(k[b, cols, kv], dtype=np.float64)
+    vv = np.asarray(v[b, cols, kv], dtype=np.float64)
     dd = np.asarray(do[b, rows, h], dtype=np.float64)
     S = (qq @ kk.T) * sc
-    M = eviction_mask(e[b], rows, n_keys)
     S = np.where(M, S, -np.inf)
     empty = ~M.any(axis=1, keepdims=True)              # rows that see no key: P = 0
-    m = np.where(empty, 0.0, S.max(axis=1, keepdims=True))
+    m = np.where(empty, 0.0, S.max(axis=1, keepdims=True, initial=-np.inf))
     Pu = np.exp(S - m)
     P = Pu / np.where(empty, 1.0, Pu.sum(axis=1, keepdims=True))   # softmax over live keys
     dP = dd @ vv.T                                     # dP_ij = dO_i . v_j
     Di = (P * dP).sum(axis=1, keepdims=True)           # sum_j P_ij dP_ij
     dS = P * (dP - Di)
-    return qq, kk, dd, P, dS, sc, n_keys, kv
+    return qq, kk, dd, P, dS, sc, cols, kv
 
 
 def attn_bwd(q, k, v, e, do, scale=None, row_chunk=512):
@@ -182,11 +190,11 @@ def attn_bwd(q, k, v, e, do, scale=None, row_chunk=512):
         for h in range(Hq):
             for i0 in range(0, N, row_chunk):
                 rows = np.arange(i0, min(N, i0 + row_chunk))
-                qq, kk, dd, P, dS, sc, nk, kv = _bwd_rows_core(
+                qq, kk, dd, P, dS, sc, cols, kv = _bwd_rows_core(
                     q, k, v, e, do, b, h, rows, scale)
                 dq[b, rows, h] = sc * (dS @ kk)
-                dk[b, :nk, kv] += sc * (dS.T @ qq)
-                dv[b, :nk, kv] += P.T @ dd
+                dk[b, cols, kv] += sc * (dS.T @ qq)
+                dv[b, cols, kv] += P.T @ dd
     return dq, dk, dv
 
 
@@ -215,10 +223,15 @@ def attn_bwd_keys(q, k, v, e, do, b, kv, keys, scale=None, row_chunk=512):
     for h in range(kv * G, (kv + 1) * G):
         for i0 in range(r0, r1, row_chunk):
             rows = np.arange(i0, min(r1, i0 + row_chunk))
-            qq, kk, dd, P, dS, sc, nk, _ = _bwd_rows_core(
+            qq, kk, dd, P, dS, sc, cols, _ = _bwd_rows_core(
                 q, k, v, e, do, b, h, rows, scale)
-            sel = keys[keys < nk]
-            idx = np.nonzero(keys < nk)[0]
+            # the requested keys among the formed columns (the others have
+            # no live query in these rows)
+            at = np.searchsorted(cols, keys)
+            hit = at < len(cols)
+            hit[hit] = cols[at[hit]] == keys[hit]
+            idx = np.flatnonzero(hit)
+            sel = at[idx]
             dk[idx] += sc * (dS[:, sel].T @ qq)
             dv[idx] += P[:, sel].T @ dd
     return dk, dv

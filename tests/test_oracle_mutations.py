@@ -22,8 +22,8 @@ MUTANTS = [
      "x1 * c + x2 * s, x2 * c - x1 * s", 1),
     ("RoPE frequency exponent", "-2.0 * kk / D", "-1.0 * kk / D", 1),
     ("dS drops the D_i term", "dS = P * (dP - Di)", "dS = P * dP", 1),
-    ("dK uses P instead of dS", "dk[b, :nk, kv] += sc * (dS.T @ qq)",
-     "dk[b, :nk, kv] += sc * (P.T @ qq)", 1),
+    ("dK uses P instead of dS", "dk[b, cols, kv] += sc * (dS.T @ qq)",
+     "dk[b, cols, kv] += sc * (P.T @ qq)", 1),
     ("GQA maps heads round robin", "kv = h // (Hq // Hkv)", "kv = h % Hkv", 2),
     ("compaction keeps block 0 always", "if keep[b][x]]", "if keep[b][x] or x == 0]", 1),
     ("decode reads one token too many", "[:L]", "[:L + 1]", 2),
