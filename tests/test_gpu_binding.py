@@ -136,9 +136,13 @@ def test_empty_inputs_are_no_ops():
     out, lse = ks.ks_paged_decode(q, empty_pool, empty_pool, tz, lens)
     pos1 = torch.full((3,), 100, dtype=torch.int32, device=DEV)
     out_r, lse_r = ks.ks_paged_decode_rope(q, pos1, empty_pool, empty_pool, tz, lens)
+    # the workspace the binding passes is exactly the C query's size for an
+    # empty table (one split per sequence and head)
+    empty_tok = torch.empty(0, Hkv, D, dtype=bf, device=DEV)
+    out_1, lse_1 = ks.ks_paged_decode_bs1(q, empty_tok, empty_tok, tz, lens)
     torch.cuda.synchronize()
     assert torch.all(nz_out == 0) and torch.all(nz_out2 == 0)
-    for o_, l_ in ((out, lse), (out_r, lse_r)):
+    for o_, l_ in ((out, lse), (out_r, lse_r), (out_1, lse_1)):
         assert torch.all(o_ == 0)
         assert torch.all(torch.isinf(l_)) and torch.all(l_ < 0)
     # entries present but no pool blocks: refused before launching

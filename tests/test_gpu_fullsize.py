@@ -7,7 +7,8 @@ import torch
 
 import kv_cache_compaction_amd as ks
 import oracle as O
-from parity_util import announce, f64, gate
+import rounding_model as RM
+from parity_util import announce, f64, gate, gate_rows_model, oracle_bwd_keys
 from workloads import (SUMMARY_32K, build_trace, check_trace, config_trace_batch,
                        normal_tensor, stacked_e)
 
@@ -29,7 +30,28 @@ def _sample_rows(tr, rng, n=40):
     return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
+def check_rows(o, lse, dq, q_raw, k_raw, v_h, do_h, e, b, hkv, rows, tag=""):
+    """Forward and dQ rows of one (trace, kv group) against the oracle; the
+    dQ gate is tied to the rounding model (parity_util.gate_rows_model)."""
+    N = q_raw.shape[1]
+    G = q_raw.shape[2]
+    qs = O.rope(q_raw, np.arange(N)[None])
+    kk = O.rope(k_raw, np.arange(N)[None])
+    eb = e[b:b + 1]
+    for hh in range(G):
+        h = hkv * G + hh
+        ro, rl = O.attn_fwd_rows(qs, kk, v_h, eb, 0, hh, rows)
+        gate(o[b, rows, h], ro, "bf16", f"O rows{tag} h{h}")
+        gate(lse[b, h, rows], rl, "bf16", f"LSE rows{tag} h{h}")
+        rdq = O.attn_bwd_rows(qs, kk, v_h, eb, do_h, 0, hh, rows)
+        mdq = RM.dq_rows(qs, kk, v_h, eb, do_h, 0, hh, rows)
+        gate_rows_model(dq[b, rows, h], rdq, mdq, f"dQ rows{tag} h{h}")
+    return qs, kk
+
+
 def run_training_config(cfg, b, hkv, key_blocks):
+    """The bench's launch on the full configuration; rows of every (trace,
+    kv group) unit and key blocks of unit (b, hkv) against the oracle."""
     traces, seeds = config_trace_batch(cfg)
     e = stacked_e(traces)
     B, N, Hq, Hkv, D = cfg.batch, cfg.N, cfg.Hq, cfg.Hkv, cfg.D
@@ -39,12 +61,8 @@ def run_training_config(cfg, b, hkv, key_blocks):
     k = normal_tensor((B, N, Hkv, D), seeds["k"], cfg.value_scale, bf, DEV)
     v = normal_tensor((B, N, Hkv, D), seeds["v"], cfg.value_scale, bf, DEV)
     do = normal_tensor((B, N, Hq, D), seeds["do"], cfg.value_scale, bf, DEV)
-    heads = slice(hkv * G, (hkv + 1) * G)
-    # raw projections of the sampled (trace, kv group) for the oracle
-    q_raw = f64(q[b:b + 1, :, heads])
-    k_raw = f64(k[b:b + 1, :, hkv:hkv + 1])
-    v_h = f64(v[b:b + 1, :, hkv:hkv + 1])
-    do_h = f64(do[b:b + 1, :, heads])
+    # raw (unrotated) projections stay on the host for the oracle
+    q_raw, k_raw = q.cpu(), k.cpu()
     pos = torch.arange(N, dtype=torch.int32, device=DEV)[None].repeat(B, 1).contiguous()
     ks.ks_rope_logical(q, k, pos)
     eg = torch.from_numpy(e).to(DEV)
@@ -66,29 +84,51 @@ def run_training_config(cfg, b, hkv, key_blocks):
     noise = 2.0**-9 * (a.square().sum().sqrt().item() + c.square().sum().sqrt().item())
     assert abs(lhs - rhs) <= 8 * noise, (lhs, rhs, noise)
 
-    tr = traces[b]
-    rows = _sample_rows(tr, np.random.default_rng(5))
-    qs = O.rope(q_raw, np.arange(N)[None])
-    kk = O.rope(k_raw, np.arange(N)[None])
-    eb = e[b:b + 1]
-    for hh in range(G):
-        ro, rl = O.attn_fwd_rows(qs, kk, v_h, eb, 0, hh, rows)
-        gate(o[b, rows, hkv * G + hh], ro, "bf16", f"O rows h{hh}")
-        gate(lse[b, hkv * G + hh, rows], rl, "bf16", f"LSE rows h{hh}")
-        rdq = O.attn_bwd_rows(qs, kk, v_h, eb, do_h, 0, hh, rows)
-        gate(dq[b, rows, hkv * G + hh], rdq, "bf16grad", f"dQ rows h{hh}")
-    for keys in key_blocks(tr):
-        rdk, rdv = O.attn_bwd_keys(qs, kk, v_h, eb, do_h, 0, 0, keys)
-        gate(dk[b, keys, hkv], rdk, "bf16grad", f"dK keys {keys[0]}..")
-        gate(dv[b, keys, hkv], rdv, "bf16grad", f"dV keys {keys[0]}..")
+    o, lse, dq, dk, dv, v_c, do_c = (t.cpu() for t in (o, lse, dq, dk, dv, v, do))
+    # rows of every (trace, kv group) unit: the structural rows plus random
+    # ones (40 for the unit whose keys are checked, 8 elsewhere)
+    for bb in range(B):
+        for gg in range(Hkv):
+            heads = slice(gg * G, (gg + 1) * G)
+            main = (bb, gg) == (b, hkv)
+            rows = _sample_rows(traces[bb], np.random.default_rng(5 + 100 * bb + gg),
+                                n=40 if main else 8)
+            qs, kk = check_rows(o, lse, dq, f64(q_raw[bb:bb + 1, :, heads]),
+                                f64(k_raw[bb:bb + 1, :, gg:gg + 1]),
+                                f64(v_c[bb:bb + 1, :, gg:gg + 1]),
+                                f64(do_c[bb:bb + 1, :, heads]), e, bb, gg, rows,
+                                tag=f" t{bb}")
+            if not main:
+                continue
+            v_h = f64(v_c[bb:bb + 1, :, gg:gg + 1])
+            do_h = f64(do_c[bb:bb + 1, :, heads])
+            blocks = key_blocks(traces[bb])
+            rdk, rdv = oracle_bwd_keys(qs, kk, v_h, e[bb:bb + 1], do_h, np.concatenate(blocks))
+            at = 0
+            for keys in blocks:
+                sl = slice(at, at + len(keys))
+                at += len(keys)
+                gate(dk[bb, keys, gg], rdk[sl], "bf16grad", f"dK t{bb} keys {keys[0]}..")
+                gate(dv[bb, keys, gg], rdv[sl], "bf16grad", f"dV t{bb} keys {keys[0]}..")
+
+
+def summary_key_blocks(tr):
+    """Key blocks whose dK/dV sum over the longest and the event-crossing
+    query ranges: the never-evicted prompt (every row of the trace), the
+    block retained at the first event and evicted at the second (its queries
+    span the first event), the trace's last keys, and a block evicted at
+    the first event."""
+    t1 = tr.events[0]
+    keep = tr.overlap + tr.summary
+    return [np.arange(0, 64),                                   # prompt: rows [0, N)
+            np.arange(tr.P - 64, tr.P),                         # prompt, last block
+            np.arange(t1 - 64, t1),                             # kept at t1, evicted later
+            np.arange(tr.N - 64, tr.N),                         # queries [j, N)
+            np.arange(t1 - keep - 64, t1 - keep)]               # evicted at t1
 
 
 def test_summary_32k_sampled():
-    def key_blocks(tr):
-        t1 = tr.events[0]
-        return [np.arange(tr.N - 64, tr.N),                      # queries [j, N)
-                np.arange(t1 - 1536 - 64, t1 - 1536)]            # evicted at t1
-    run_training_config(SUMMARY_32K, b=1, hkv=3, key_blocks=key_blocks)
+    run_training_config(SUMMARY_32K, b=1, hkv=3, key_blocks=summary_key_blocks)
 
 
 def test_trace_past_one_live_window():
@@ -128,7 +168,8 @@ def test_trace_past_one_live_window():
         gate(o[0, rows, hkv * G + hh], ro, "bf16", f"O rows h{hh}")
         gate(lse[0, hkv * G + hh, rows], rl, "bf16", f"LSE rows h{hh}")
         rdq = O.attn_bwd_rows(qh, kh, vh, e64, doh, 0, hh, rows)
-        gate(dq[0, rows, hkv * G + hh], rdq, "bf16grad", f"dQ rows h{hh}")
+        mdq = RM.dq_rows(qh, kh, vh, e64, doh, 0, hh, rows)
+        gate_rows_model(dq[0, rows, hkv * G + hh], rdq, mdq, f"dQ rows h{hh}")
     for keys in (np.arange(N - 64, N), np.arange(w - 32, w + 32)):
         rdk, rdv = O.attn_bwd_keys(qh, kh, vh, e64, doh, 0, 0, keys)
         gate(dk[0, keys, hkv], rdk, "bf16grad", f"dK keys {keys[0]}..")

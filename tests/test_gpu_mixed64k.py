@@ -9,7 +9,8 @@ import torch
 
 import kv_cache_compaction_amd as ks
 import oracle as O
-from parity_util import announce, f64, gate
+import rounding_model as RM
+from parity_util import announce, f64, gate, gate_rows_model, oracle_bwd_keys
 from workloads import (BLOCK, KS_NEVER, LONG_MIXED_64K, config_trace_batch, evict_units,
                        normal_tensor, stacked_e)
 
@@ -93,16 +94,40 @@ def test_mixed64k_sampled_rows_and_keys(run, b):
         gate(run["o"][b, rows, h], ro, "bf16", f"O rows t{b} h{h}")
         gate(run["lse"][b, h, rows], rl, "bf16", f"LSE rows t{b} h{h}")
         rdq = O.attn_bwd_rows(qs, kk, r["v"], eb, r["do"], 0, hh, rows)
-        gate(run["dq"][b, rows, h], rdq, "bf16grad", f"dQ rows t{b} h{h}")
-    blocks = [np.arange(N - 64, N)]
+        mdq = RM.dq_rows(qs, kk, r["v"], eb, r["do"], 0, hh, rows)
+        gate_rows_model(run["dq"][b, rows, h], rdq, mdq, f"dQ rows t{b} h{h}")
+    blocks = key_blocks(tr)
+    rdk, rdv = oracle_bwd_keys(qs, kk, r["v"], eb, r["do"], np.concatenate(blocks))
+    at = 0
+    for keys in blocks:
+        sl = slice(at, at + len(keys))
+        at += len(keys)
+        gate(run["dk"][b, keys, g], rdk[sl], "bf16grad", f"dK t{b} keys {keys[0]}..")
+        gate(run["dv"][b, keys, g], rdv[sl], "bf16grad", f"dV t{b} keys {keys[0]}..")
+
+
+def key_blocks(tr):
+    """Key blocks of one trace whose dK/dV sum over the longest and the
+    event-crossing query ranges: the prompt's first and last blocks (every
+    row of the trace where the prompt is pinned; up to the event that pops
+    it in the sliding window), a block alive across the first event and
+    evicted later, the trace's last keys, and for the summary strategy a
+    block evicted at the first event."""
+    N, P = tr.N, tr.P
+    t1 = tr.events[0]
+    blocks = [np.arange(0, 64), np.arange(P - 64, P)]
+    for j0 in range(t1 - 64, P - 1, -64):         # alive across t1, evicted later
+        ej = tr.e[j0:j0 + 64].astype(np.int64)
+        if ej.min() > t1 and ej.max() < N:
+            blocks.append(np.arange(j0, j0 + 64))
+            break
+    else:
+        raise AssertionError("no block alive across the first event")
+    blocks.append(np.arange(N - 64, N))
     if tr.strategy == "summary":
-        t1 = tr.events[0]
         lo = t1 - (tr.overlap + tr.summary)
         blocks.append(np.arange(lo - 64, lo))       # evicted at the first event
-    for keys in blocks:
-        rdk, rdv = O.attn_bwd_keys(qs, kk, r["v"], eb, r["do"], 0, 0, keys)
-        gate(run["dk"][b, keys, g], rdk, "bf16grad", f"dK t{b} keys {keys[0]}..")
-        gate(run["dv"][b, keys, g], rdv, "bf16grad", f"dV t{b} keys {keys[0]}..")
+    return blocks
 
 
 def test_mixed64k_decode_with_forced_compaction(run):

@@ -9,7 +9,8 @@ import torch
 
 import kv_cache_compaction_amd as ks
 import oracle as O
-from parity_util import announce, f64, gate
+import rounding_model as RM
+from parity_util import announce, f64, gate, gate_rows_model
 from workloads import (SUMMARY_32K, TRAIN_4K, config_trace_batch, normal_tensor, reprefill_pack,
                        reprefill_segments)
 
@@ -92,7 +93,8 @@ def test_reprefill_32k_sampled():
         gate(o[b, rows, g * G + hh], ro, "bf16", f"O rows h{hh}")
         gate(lse[b, g * G + hh, rows], rl, "bf16", f"LSE rows h{hh}")
         rdq = O.attn_bwd_rows(q, k, v, en, do, 0, hh, rows)
-        gate(dq[b, rows, g * G + hh], rdq, "bf16grad", f"dQ rows h{hh}")
+        mdq = RM.dq_rows(q, k, v, en, do, 0, hh, rows)
+        gate_rows_model(dq[b, rows, g * G + hh], rdq, mdq, f"dQ rows h{hh}")
     for keys in (np.arange(0, 64), np.arange(n - 64, n)):
         rdk, rdv = O.attn_bwd_keys(q, k, v, en, do, 0, 0, keys)
         gate(dk[b, keys, g], rdk, "bf16grad", f"dK keys {keys[0]}..")

@@ -188,3 +188,15 @@ def test_decode_pool_must_have_blocks_when_entries_exist(lib):
     st, msg = _status(lib, "ks_paged_decode", FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 32, 8,
                       128, 10, 4, 1, 0.1, FAKE, need, None)
     assert st == 1 and "null" in msg
+
+
+def test_decode_workspace_query_covers_empty_tables(lib):
+    """A table with no entries still launches one split per (sequence, head):
+    the size query must cover it, so a C caller that sizes the workspace by
+    the query gets no KS_ERR_WORKSPACE on the empty-table case."""
+    for fn in ("ks_paged_decode_workspace", "ks_paged_decode_bs1_workspace"):
+        one = getattr(lib, fn)(4, 32, 128, 1)
+        assert one > 0
+        assert getattr(lib, fn)(4, 32, 128, 0) == one
+        assert getattr(lib, fn)(4, 32, 128, -3) == one
+        assert getattr(lib, fn)(0, 32, 128, 0) == 0
