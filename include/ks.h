@@ -233,6 +233,9 @@ ks_status ks_compact_block_table_rounds(const int32_t* table_in,
  *          sequence yields a zero output and lse = -inf
  * out      [B, Hq, D] bf16;  lse float [B, Hq] natural log, may be NULL
  * dtype    KS_BF16; D = 128.
+ * ws       at least ks_paged_decode_workspace(B, Hq, D, max_blocks) bytes
+ *          (split partials); with max_blocks = 0 the query returns the size
+ *          of one split, which the call still needs.
  */
 size_t ks_paged_decode_workspace(int B, int Hq, int D, int max_blocks);
 ks_status ks_paged_decode(const void* q, const void* k_pool,

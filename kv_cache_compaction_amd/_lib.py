@@ -294,7 +294,7 @@ def ks_paged_decode(q, k_pool, v_pool, table, seq_lens, scale=None, out=None, ls
     out = torch.empty_like(q) if out is None else _given("out", out, q.shape, q.dtype)
     lse = (torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None
            else _given("lse", lse, (B, Hq), torch.float32))
-    nbytes = lib.ks_paged_decode_workspace(B, Hq, D, max(MB, 1))
+    nbytes = lib.ks_paged_decode_workspace(B, Hq, D, MB)
     ws = _workspace(nbytes, q.device, ws)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     st = lib.ks_paged_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(table), _ptr(seq_lens),
@@ -353,7 +353,7 @@ def ks_paged_decode_bs1(q, k_pool, v_pool, token_table, seq_lens, scale=None, ou
     out = torch.empty_like(q) if out is None else _given("out", out, q.shape, q.dtype)
     lse = (torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None
            else _given("lse", lse, (B, Hq), torch.float32))
-    nbytes = lib.ks_paged_decode_bs1_workspace(B, Hq, D, max(MT, 1))
+    nbytes = lib.ks_paged_decode_bs1_workspace(B, Hq, D, MT)
     ws = _workspace(nbytes, q.device, ws)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     st = lib.ks_paged_decode_bs1(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(token_table),
@@ -447,8 +447,8 @@ def ks_paged_decode_rope(q, pos, k_pool, v_pool, table, seq_lens, base=10000.0, 
     out = torch.empty_like(q) if out is None else _given("out", out, q.shape, q.dtype)
     lse = (torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None
            else _given("lse", lse, (B, Hq), torch.float32))
-    nbytes = (lib.ks_paged_decode_workspace(B, Hq, D, max(ME, 1)) if BS == KS_BLOCK
-              else lib.ks_paged_decode_bs1_workspace(B, Hq, D, max(ME, 1)))
+    nbytes = (lib.ks_paged_decode_workspace(B, Hq, D, ME) if BS == KS_BLOCK
+              else lib.ks_paged_decode_bs1_workspace(B, Hq, D, ME))
     ws = _workspace(nbytes, q.device, ws)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     st = lib.ks_paged_decode_rope(_ptr(q), _ptr(pos), _ptr(k_pool), _ptr(v_pool), _ptr(table),

@@ -153,6 +153,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       sacc = mfma16x16x32(qa[s], __builtin_bit_cast(bf16x8, r.k[s]), sacc);
+    // The scores are read by VALU code below, on both sides of the tail-block
+    // branch.  The hardware does not interlock an MFMA result with a VALU
+    // read: v_mfma_f32_16x16x32_bf16 needs 8 independent wait states first
+    // (the gfx950 backend's own requirement for this instruction).  They
+    // are issued explicitly here, fenced so that no read can move above them,
+    // instead of relying on the compiler's placement across the branch.
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
     const bool valid = blk * 16 + t < L;
     if ((blk + 1) * 16 > L) {  // tail block: slots past L may hold anything
 #pragma unroll
@@ -426,8 +435,10 @@ ks_status append_impl(const char* name, const void* k_new, const void* v_new,
 
 }  // namespace
 
+// A table row with no entries still gets the one-split workspace the launch
+// asks for (every length clamps to 0 and the reduce writes the empty rows).
 extern "C" size_t ks_paged_decode_workspace(int B, int Hq, int Dh, int max_blocks) {
-  return decode_workspace(B, Hq, Dh, max_blocks);
+  return decode_workspace(B, Hq, Dh, max_blocks > 0 ? max_blocks : 1);
 }
 
 extern "C" ks_status ks_paged_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -441,8 +452,7 @@ extern "C" ks_status ks_paged_decode(const void* q, const void* k_pool, const vo
 }
 
 extern "C" size_t ks_paged_decode_bs1_workspace(int B, int Hq, int Dh, int max_tokens) {
-  if (max_tokens <= 0) return 0;
-  return decode_workspace(B, Hq, Dh, (max_tokens + 15) / 16);
+  return decode_workspace(B, Hq, Dh, max_tokens > 0 ? (max_tokens + 15) / 16 : 1);
 }
 
 extern "C" ks_status ks_paged_decode_bs1(const void* q, const void* k_pool, const void* v_pool,
