@@ -323,6 +323,36 @@ ks_status ks_paged_decode_rope(const void* q, const int32_t* pos,
                                void* stream);
 
 /*
+ * ks_paged_decode_noalloc -- ks_paged_decode for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  No workspace argument: the split partials live in a
+ * device array owned by the library, ks_paged_decode_noalloc_max_scratch()
+ * bytes (96 MiB) per GPU, kept until the process ends.  The call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *
+ * Limit   B * Hq * ceil(max_blocks / 48) split slots of (D + 2) floats must
+ *         fit the array (e.g. 64 sequences x 32 query heads over tables of
+ *         4,096 blocks); larger calls return KS_ERR_WORKSPACE before any
+ *         launch -- use ks_paged_decode with a workspace for those.
+ * Sharing Every call on one GPU uses that GPU's single array, which keeps the
+ *         last call's contents (each call writes every entry it reads).
+ *         Calls that overlap in time on one GPU -- on different streams or
+ *         from different host threads -- RACE and may return wrong results;
+ *         serialize them (one stream, or events between streams).
+ * The first call on a device looks up that device's array (the device of
+ * `stream`, or the current device for the null stream); a failure there
+ * returns KS_ERR_HIP.  Arguments, outputs and other errors as for
+ * ks_paged_decode; results are bit-identical to it.
+ */
+size_t ks_paged_decode_noalloc_max_scratch(void);
+ks_status ks_paged_decode_noalloc(const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* table,
+                                  const int32_t* seq_lens, void* out, float* lse,
+                                  int B, int Hq, int Hkv, int D, int max_blocks,
+                                  int num_pool_blocks, int dtype, float scale,
+                                  void* stream);
+
+/*
  * ks_append_kv_bs1 -- ks_append_kv with single-token blocks: the new token's
  * rotated key and its value go to pool slot token_table[b][seq_lens[b] - 1].
  *

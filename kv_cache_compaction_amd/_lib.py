@@ -46,6 +46,8 @@ _SIGS = {
     "ks_compact_block_table_rounds": ([_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp], _i),
     "ks_paged_decode_workspace": ([_i, _i, _i, _i], _sz),
     "ks_paged_decode": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+    "ks_paged_decode_noalloc_max_scratch": ([], _sz),
+    "ks_paged_decode_noalloc": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
     "ks_append_kv": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _f, _vp], _i),
     "ks_paged_decode_bs1_workspace": ([_i, _i, _i, _i], _sz),
     "ks_paged_decode_bs1": ([_vp] * 7 + [_i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
@@ -301,6 +303,38 @@ def ks_paged_decode(q, k_pool, v_pool, table, seq_lens, scale=None, out=None, ls
                              _ptr(out), _ptr(lse), B, Hq, Hkv, D, MB, NB, _dtype_code(q), sc,
                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("ks_paged_decode", st)
+    return out, lse
+
+
+def ks_paged_decode_noalloc_max_scratch():
+    return load_library().ks_paged_decode_noalloc_max_scratch()
+
+
+def ks_paged_decode_noalloc(q, k_pool, v_pool, table, seq_lens, scale=None, out=None, lse=None,
+                            stream=None):
+    """ks_paged_decode with the library's own per-GPU scratch (no workspace).
+    Returns (out, lse); pass out and lse to keep the call allocation-free."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    _need(k_pool.dim() == 4, "pool must be [NB, Hkv, 16, D]")
+    NB, Hkv, BS, Dp = k_pool.shape
+    _need(BS == KS_BLOCK and Dp == D, "pool must be [NB, Hkv, 16, D] with q's D")
+    _cuda_contig("q", q)
+    _cuda_contig("k_pool", k_pool, q.dtype)
+    _cuda_contig("v_pool", v_pool, q.dtype)
+    _cuda_contig("table", table, torch.int32)
+    _cuda_contig("seq_lens", seq_lens, torch.int32)
+    _need(tuple(v_pool.shape) == tuple(k_pool.shape), "v_pool shape")
+    _need(table.shape[0] == B and tuple(seq_lens.shape) == (B,), "table/seq_lens shape")
+    MB = table.shape[1]
+    out = torch.empty_like(q) if out is None else _given("out", out, q.shape, q.dtype)
+    lse = (torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None
+           else _given("lse", lse, (B, Hq), torch.float32))
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.ks_paged_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(table),
+                                     _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, MB, NB,
+                                     _dtype_code(q), sc, _stream(stream))
+    _check("ks_paged_decode_noalloc", st)
     return out, lse
 
 

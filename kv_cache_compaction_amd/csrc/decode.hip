@@ -39,6 +39,8 @@
 // head groups fastest, so the Hkv waves reading the slices of one pool block
 // (Hkv x 16 x D contiguous elements of K, and of V) run side by side, which
 // keeps the DRAM accesses of concurrent waves on the same rows.
+#include <mutex>
+
 #include "ks_common.h"
 
 namespace {
@@ -499,4 +501,76 @@ extern "C" ks_status ks_append_kv_bs1(const void* k_new, const void* v_new, cons
                                       void* stream) {
   return append_impl<1>("ks_append_kv_bs1", k_new, v_new, pos, token_table, seq_lens, k_pool,
                         v_pool, B, Hkv, Dh, max_tokens, num_pool_tokens, dtype, base, stream);
+}
+
+// ---------------------------------------------------------------------------
+// ks_paged_decode_noalloc: ks_paged_decode with its split partials kept in a
+// device array the library owns, for callers that cannot allocate.  The
+// array lives for the whole process on every GPU the library runs on; one
+// copy per device, found once per device with hipGetSymbolAddress (in host
+// code `scratch` names a host-side stand-in, never the device memory).
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t{96} << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// the device address of this device's scratch array (looked up on the first
+// call on that device, with that device current)
+static ks_status scratch_on(hipStream_t stream, const char* name, void** out) {
+  int dev = -1;
+  hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (err != hipSuccess)
+    return ks_fail(KS_ERR_HIP, "%s: device of the stream: %s", name, hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return ks_fail(KS_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", name,
+                   dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    int cur = -1;
+    err = hipGetDevice(&cur);
+    if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+    void* p = nullptr;
+    if (err == hipSuccess) err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (err == hipSuccess) err = back;
+    }
+    if (err != hipSuccess || !p)
+      return ks_fail(KS_ERR_HIP, "%s: scratch address on device %d: %s", name, dev,
+                     hipGetErrorString(err));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return KS_OK;
+}
+
+extern "C" size_t ks_paged_decode_noalloc_max_scratch(void) { return kScratchBytes; }
+
+extern "C" ks_status ks_paged_decode_noalloc(const void* q, const void* k_pool,
+                                             const void* v_pool, const int32_t* table,
+                                             const int32_t* seq_lens, void* out, float* lse,
+                                             int B, int Hq, int Hkv, int Dh, int max_blocks,
+                                             int num_pool_blocks, int dtype, float scale,
+                                             void* stream) {
+  const char* name = "ks_paged_decode_noalloc";
+  if (B > 0 && Hq > 0 && Dh > 0) {
+    const size_t need = decode_workspace(B, Hq, Dh, max_blocks > 0 ? max_blocks : 1);
+    if (need > kScratchBytes)
+      return ks_fail(KS_ERR_WORKSPACE,
+                     "%s: needs %zu bytes of split partials (B=%d, Hq=%d, max_blocks=%d), "
+                     "more than its %zu-byte scratch; use ks_paged_decode with a workspace",
+                     name, need, B, Hq, max_blocks, kScratchBytes);
+  }
+  void* ws = nullptr;
+  if (B > 0) {
+    const ks_status st = scratch_on(static_cast<hipStream_t>(stream), name, &ws);
+    if (st != KS_OK) return st;
+  }
+  return decode_impl<16>(name, q, k_pool, v_pool, table, seq_lens, out, lse, B, Hq, Hkv, Dh,
+                         max_blocks, num_pool_blocks, dtype, scale, ws, kScratchBytes, stream);
 }
