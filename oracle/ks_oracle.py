@@ -94,24 +94,28 @@ def _scale(D, scale):
 def attn_fwd_rows(q, k, v, e, b, h, rows, scale=None):
     """Output rows ``rows`` of query head ``h`` of trace ``b``.
 
-    Returns (o [len(rows), D], lse [len(rows)]).  S_ij = scale q_i.k_j with
-    j running over the whole causal prefix, masked by M; LSE_i = log sum_M
-    exp S_ij; O_i = sum_M exp(S_ij - LSE_i) v_j.
+    Returns (o [len(rows), D], lse [len(rows)]).  S_ij = scale q_i.k_j over
+    the keys j of the causal prefix, masked by M; LSE_i = log sum_M exp S_ij;
+    O_i = sum_M exp(S_ij - LSE_i) v_j.  Only the key columns live for at
+    least one of the rows are formed (a column masked in every row adds
+    nothing to any sum); the mask is applied element by element inside them.
     """
     Hq, Hkv, D = q.shape[2], k.shape[2], q.shape[3]
     kv = h // (Hq // Hkv)
     rows = np.asarray(rows, dtype=np.int64)
     n_keys = int(rows.max()) + 1
-    qq = np.asarray(q[b, rows, h], dtype=np.float64)
-    kk = np.asarray(k[b, :n_keys, kv], dtype=np.float64)
-    vv = np.asarray(v[b, :n_keys, kv], dtype=np.float64)
-    S = (qq @ kk.T) * _scale(D, scale)
     M = eviction_mask(e[b], rows, n_keys)
+    cols = np.flatnonzero(M.any(axis=0))
+    M = M[:, cols]
+    qq = np.asarray(q[b, rows, h], dtype=np.float64)
+    kk = np.asarray(k[b, cols, kv], dtype=np.float64)
+    vv = np.asarray(v[b, cols, kv], dtype=np.float64)
+    S = (qq @ kk.T) * _scale(D, scale)
     S = np.where(M, S, -np.inf)
     # a row that sees no key (only possible when a record breaks e_j > j)
     # is an empty softmax: O = 0, LSE = -inf
     empty = ~M.any(axis=1, keepdims=True)
-    m = np.where(empty, 0.0, S.max(axis=1, keepdims=True))
+    m = np.where(empty, 0.0, S.max(axis=1, keepdims=True, initial=-np.inf))
     Pu = np.exp(S - m)
     l = Pu.sum(axis=1, keepdims=True)
     with np.errstate(divide="ignore"):
