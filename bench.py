@@ -202,6 +202,10 @@ def main():
     do = normal_tensor((B, N, Hq, D), seeds["do"], trn.value_scale, bf, dev)
     e = torch.from_numpy(e_np).to(dev)
     pos = torch.arange(N, dtype=torch.int32, device=dev)[None].repeat(B, 1).contiguous()
+    # every step rotates fresh copies of the raw projections (ks_rope_logical
+    # works in place), so the timed attention always runs on the inputs the
+    # tests check; the copies are made outside the timed stages
+    q_raw, k_raw = q.clone(), k.clone()
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -260,6 +264,8 @@ def main():
         def t1(ev, name):
             if tm:
                 tm.stop(ev, name)
+        q.copy_(q_raw)
+        k.copy_(k_raw)
         ev = t0()
         ks.ks_rope_logical(q, k, pos, stream=stream)
         t1(ev, "rope")
@@ -396,6 +402,13 @@ def main():
         "stages": {kk: {x: (round(y, 4) if isinstance(y, float) else y) for x, y in vv.items()}
                    for kk, vv in parts.items()},
     }
+    mfma = mfma_rate(ks, torch, stream)
+    result["mfma_reference"] = mfma
+    result["roofline"]["peak_measured"] = mfma["tflops"]
+    result["roofline"]["frac_of_measured"] = round(parts[dom]["achieved"] / mfma["tflops"], 4)
+    for p in parts.values():
+        if p["bound"] == "mfma":
+            p["frac_of_measured"] = round(p["achieved"] / mfma["tflops"], 4)
     result["hbm_reference"] = hbm_reference(torch, stream)
     result["single_token_blocks"] = token_granular_decode(ks, torch, stream, dec)
     result["toy_stack"] = toy_stack_mismatch(torch)
@@ -403,7 +416,15 @@ def main():
         ks, torch, traces, q, k, v, do, stream, ms, pairs, trn)
     result["long_mixed_64k"] = long_mixed_64k(ks, torch, stream)
     if not args.no_cpu_baseline:
+        small = small_configs_gpu(ks, torch, stream)
         result["cpu_baseline"] = cpu_baseline(traces, seeds, trn, args.cpu_seconds)
+        dec_gpu = dict(db=db, kp=kp, vp=vp, q=q4[:, 0], k_new=k4, v_new=v4, pos=db.pos,
+                       out=out4, lse=lse4, table=tbufs[0], ms=ms["compact"] + ms["decode"])
+        result["cpu_baseline"]["per_config"] = cpu_per_config(
+            small, result["cpu_baseline"], traces, trn, ms["rope"] + attn_ms, dec_gpu,
+            result["long_mixed_64k"])
+        for key in ("_n", "_heads", "_seconds"):
+            result["cpu_baseline"].pop(key)
     print(json.dumps(result), flush=True)
 
 
@@ -669,6 +690,242 @@ def long_mixed_64k(ks, torch, stream, reps=5):
     return out
 
 
+def mfma_rate(ks, torch, stream, workgroups=2048, iters=2500):
+    """bf16 MFMA rate of a loop of nothing but 32x32x16 MFMAs at the attention
+    kernels' occupancy (8 waves per workgroup, 2 per SIMD), timed with HIP
+    events: the rate this GPU sustains at the clock it holds under such a
+    load, beside the published dense peak."""
+    seed = torch.full((1024,), 0.01, dtype=torch.bfloat16, device="cuda")
+    sink = torch.empty(workgroups * 512, dtype=torch.float32, device="cuda")
+    run = lambda: ks.ks_measure_mfma_bf16(seed, sink, workgroups, iters, stream=stream)
+    run()
+    torch.cuda.synchronize()
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = ks.ks_measure_mfma_flops(workgroups, iters)
+    return {"what": "v_mfma_f32_32x32x16_bf16 only, 4 independent chains per wave, "
+                    "2 waves per SIMD", "workgroups": workgroups, "ms": round(ms, 3),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_published_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                            4)}
+
+
+def _median_ms(torch, stream, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1))
+    return float(np.median(t))
+
+
+def small_configs_gpu(ks, torch, stream, reps=20):
+    """The two small workloads on the GPU, timed (median of reps) and kept
+    for the oracle beside them: the 512-token fp32 trace (RoPE, forward,
+    compaction of its 32-block table) and the 4k bf16 trace (RoPE, forward,
+    backward).  Inputs are drawn on the host (numpy), as the tests draw them."""
+    from workloads import TINY_F32, TRAIN_4K, config_trace_batch, normal_tensor, stacked_e
+    from workloads import trace_blocks_keep
+
+    out = {}
+    for cfg in (TINY_F32, TRAIN_4K):
+        traces, seeds = config_trace_batch(cfg)
+        e_np = stacked_e(traces)
+        B, N, Hq, Hkv, D = cfg.batch, cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+        dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        raw = {nm: normal_tensor(shp, seeds[nm], cfg.value_scale, dt)
+               for nm, shp in (("q", (B, N, Hq, D)), ("k", (B, N, Hkv, D)),
+                               ("v", (B, N, Hkv, D)), ("do", (B, N, Hq, D)))}
+        g = {nm: t.cuda() for nm, t in raw.items()}
+        qg, kg = g["q"].clone(), g["k"].clone()
+        e = torch.from_numpy(e_np).cuda()
+        pos = torch.arange(N, dtype=torch.int32, device="cuda")[None].repeat(B, 1).contiguous()
+        o = torch.empty_like(qg)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+        dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(g["v"])
+        rec = {"cfg": cfg, "traces": traces, "raw": raw}
+        if cfg.backward:
+            def run():
+                qg.copy_(g["q"])
+                kg.copy_(g["k"])
+                ks.ks_rope_logical(qg, kg, pos, stream=stream)
+                ks.ks_evict_attn_fwd(qg, kg, g["v"], e, out=o, lse=lse, stream=stream)
+                ks.ks_evict_attn_bwd(qg, kg, g["v"], e, o, lse, g["do"], dq=dq, dk=dk, dv=dv,
+                                     stream=stream)
+        else:
+            perm = np.random.default_rng(7).permutation(32).astype(np.int32)[None]
+            keep = trace_blocks_keep(traces[0])[None]
+            tg, ng = torch.from_numpy(perm).cuda(), torch.tensor([32], dtype=torch.int32).cuda()
+            kpg = torch.from_numpy(keep).cuda()
+            tout, nout = torch.empty_like(tg), torch.empty_like(ng)
+            rec.update(table=perm, keep=keep)
+
+            def run():
+                qg.copy_(g["q"])
+                kg.copy_(g["k"])
+                ks.ks_rope_logical(qg, kg, pos, stream=stream)
+                ks.ks_evict_attn_fwd(qg, kg, g["v"], e, out=o, lse=lse, stream=stream)
+                ks.ks_compact_block_table(tg, ng, kpg, tout, nout, stream=stream)
+        rec["gpu_ms"] = _median_ms(torch, stream, run, reps)
+        rec["o"], rec["lse"] = o.cpu(), lse.cpu()
+        if cfg.backward:
+            rec["dq"], rec["dk"], rec["dv"] = dq.cpu(), dk.cpu(), dv.cpu()
+        else:
+            rec["table_out"], rec["n_out"] = tout.cpu().numpy(), nout.cpu().numpy()
+        out[cfg.name] = rec
+    return out
+
+
+def oracle_formed_entries(e_row, n, chunk=512):
+    """(row, key) entries the oracle forms for one query head over rows
+    [0, n) of a trace: per chunk of rows [i0, i1) it forms the key columns
+    live for some row of the chunk, {j < i1 : e_j > i0}.  Its time per head
+    follows this count, which scales a sample to a full configuration."""
+    e_row = np.asarray(e_row, dtype=np.int64)
+    tot = 0
+    for i0 in range(0, n, chunk):
+        i1 = min(n, i0 + chunk)
+        tot += (i1 - i0) * int((e_row[:i1] > i0).sum())
+    return tot
+
+
+def cpu_per_config(small, base, traces, cfg3, gpu3_ms, dec, mixed):
+    """The fp64 oracle beside the GPU on every workload: the 512-token, 4k and
+    decode workloads in full (with the GPU's error against it), the 32k and
+    64k workloads extrapolated from a sample by the oracle's formed entries."""
+    import torch
+
+    import oracle as O
+    from workloads import LONG_MIXED_64K, config_trace_batch, stacked_e
+
+    f64 = lambda t: t.to(torch.float64).numpy()
+    res = {}
+    # --- 512-token fp32 trace: RoPE, forward, compaction of its 32-block table
+    r = small["tiny-f32"]
+    c = r["cfg"]
+    e = stacked_e(r["traces"]).astype(np.int64)
+    t0 = time.perf_counter()
+    pos = np.arange(c.N)[None]
+    qr, kr = O.rope(f64(r["raw"]["q"]), pos), O.rope(f64(r["raw"]["k"]), pos)
+    ro, rl = O.attn_fwd(qr, kr, f64(r["raw"]["v"]), e)
+    rt, rn = O.compact_block_table(r["table"], np.array([32]), r["keep"])
+    el = time.perf_counter() - t0
+    res["tiny-f32"] = {
+        "work": "RoPE + masked forward of 512 fp32 tokens + compaction of a 32-block table",
+        "oracle_s": round(el, 4), "oracle_measured": "full", "gpu_ms": round(r["gpu_ms"], 4),
+        "gpu_max_abs_err": {"o": float(np.abs(f64(r["o"]) - ro).max()),
+                            "lse": float(np.abs(f64(r["lse"]) - rl).max())},
+        "table_bit_exact": bool(np.array_equal(r["table_out"], rt)
+                                and np.array_equal(r["n_out"], rn)),
+    }
+    # --- 4k bf16 trace: RoPE, forward, backward (every head)
+    r = small["train-4k"]
+    c = r["cfg"]
+    e = stacked_e(r["traces"]).astype(np.int64)
+    t0 = time.perf_counter()
+    pos = np.arange(c.N)[None]
+    qr, kr = O.rope(f64(r["raw"]["q"]), pos), O.rope(f64(r["raw"]["k"]), pos)
+    vv, dd = f64(r["raw"]["v"]), f64(r["raw"]["do"])
+    ro, rl = O.attn_fwd(qr, kr, vv, e)
+    rdq, rdk, rdv = O.attn_bwd(qr, kr, vv, e, dd)
+    el = time.perf_counter() - t0
+    err = {nm: float(np.abs(f64(r[nm]) - ref).max())
+           for nm, ref in (("o", ro), ("lse", rl), ("dq", rdq), ("dk", rdk), ("dv", rdv))}
+    res["train-4k"] = {"work": "RoPE + masked forward + backward, 4096 tokens, 8 q / 2 kv heads",
+                       "oracle_s": round(el, 3), "oracle_measured": "full",
+                       "gpu_ms": round(r["gpu_ms"], 4), "gpu_max_abs_err": err}
+    # --- 32k summary traces: from the sample the headline baseline timed
+    full = sum(oracle_formed_entries(tr.e, cfg3.N) for tr in traces) * cfg3.Hq
+    samp = oracle_formed_entries(traces[0].e, base["_n"]) * base["_heads"]
+    est = base["_seconds"] * full / samp
+    res["summary-32k"] = {
+        "work": "RoPE + masked forward + backward, 4 x 32768 tokens, 32 q / 8 kv heads",
+        "oracle_s": round(est, 1),
+        "oracle_measured": f"extrapolated from the timed sample ({base['_n']} tokens of trace 0, "
+                           f"{base['_heads']} heads: {base['_seconds']:.1f} s) by the oracle's "
+                           f"formed (row, key) entries, x{full / samp:.1f}",
+        "gpu_ms": round(gpu3_ms, 3)}
+    # --- paged decode: the step's compaction events, append, decode (all 64)
+    db = dec["db"]
+    B, MB = db.table0.shape
+    Hq, Hkv, D = dec["q"].shape[1], dec["kp"].shape[1], dec["q"].shape[2]
+    L = (db.live_len + 1).astype(np.int64)
+    t0 = time.perf_counter()
+    rt, rn = db.table0, db.nblk0
+    for x in range(db.keeps.shape[0]):
+        rt, rn = O.compact_block_table(rt, rn, db.keeps[x])
+    el_c = time.perf_counter() - t0
+    need = [rt[b, :(int(L[b]) + 15) // 16] for b in range(B)]
+    ids = np.unique(np.concatenate(need))
+    idx = torch.from_numpy(ids.astype(np.int64)).cuda()
+    kh = dec["kp"].index_select(0, idx).float().cpu().numpy()
+    vh = dec["vp"].index_select(0, idx).float().cpu().numpy()
+    where = {int(p): i for i, p in enumerate(ids)}
+    rt2 = np.full_like(rt, -1)
+    for b in range(B):
+        rt2[b, :len(need[b])] = [where[int(p)] for p in need[b]]
+    q_raw = dec["q"].float().cpu().numpy().astype(np.float64)
+    k_raw = dec["k_new"].float().cpu().numpy().astype(np.float64)
+    v_new = dec["v_new"].float().cpu().numpy()
+    t0 = time.perf_counter()
+    posd = db.pos.astype(np.int64)
+    qrot = O.rope(q_raw[:, None], posd[:, None])[:, 0]
+    krot = O.rope(k_raw[:, None], posd[:, None])[:, 0]
+    for b in range(B):                      # the append: token L-1 of each sequence
+        blk, slot = int(rt2[b, (L[b] - 1) // 16]), int((L[b] - 1) % 16)
+        kh[blk, :, slot] = krot[b]
+        vh[blk, :, slot] = v_new[b]
+    ro, rl = O.paged_decode(qrot, kh, vh, rt2, L)
+    el = el_c + time.perf_counter() - t0
+    res["paged-decode"] = {
+        "work": "1-6 compaction events + append + one decode step, 64 caches of 4k-16k tokens, "
+                "32 q / 8 kv heads",
+        "oracle_s": round(el, 3), "oracle_measured": "full",
+        "gpu_ms": round(dec["ms"], 4),
+        "gpu_max_abs_err": {"out": float(np.abs(dec["out"].float().cpu().numpy() - ro).max()),
+                            "lse": float(np.abs(dec["lse"].cpu().numpy() - rl).max())},
+        "table_bit_exact": bool(np.array_equal(dec["table"].cpu().numpy(), rt)),
+    }
+    del kh, vh
+    # --- 64k mixed: one query head of trace 0 over its first 16384 tokens
+    cfg5 = LONG_MIXED_64K
+    tr5, seeds5 = config_trace_batch(cfg5)
+    n = 16384
+    rng = np.random.default_rng(5005)
+    x = {nm: rng.standard_normal((1, n, 1, cfg5.D)) * cfg5.value_scale
+         for nm in ("q", "k", "v", "do")}
+    e5 = tr5[0].e[None, :n].astype(np.int64)
+    t0 = time.perf_counter()
+    pos = np.arange(n)[None]
+    qr, kr = O.rope(x["q"], pos), O.rope(x["k"], pos)
+    O.attn_fwd(qr, kr, x["v"], e5)
+    O.attn_bwd(qr, kr, x["v"], e5, x["do"])
+    el = time.perf_counter() - t0
+    full5 = sum(oracle_formed_entries(tr.e, cfg5.N) for tr in tr5) * cfg5.Hq
+    samp5 = oracle_formed_entries(tr5[0].e, n)
+    res["long-mixed-64k"] = {
+        "work": "masked forward + backward, 8 x 65536 tokens, 64 q / 8 kv heads",
+        "oracle_s": round(el * full5 / samp5, 1),
+        "oracle_measured": f"extrapolated from one query head over the first {n} tokens of "
+                           f"trace 0 ({el:.1f} s) by the oracle's formed (row, key) entries, "
+                           f"x{full5 / samp5:.0f}",
+        "gpu_ms": round(mixed["ms_fwd"] + mixed["ms_bwd"], 2)}
+    for v in res.values():
+        v["gpu_speedup"] = round(v["oracle_s"] * 1e3 / v["gpu_ms"], 1)
+    return res
+
+
 def cpu_baseline(traces, seeds, cfg, budget_s):
     """Time the fp64 oracle (forward + backward on a prefix of one trace, one
     query head at a time, until about budget_s seconds have passed) on the
@@ -698,7 +955,7 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
     ks.ks_rope_logical(qa, ka, torch.arange(N, dtype=torch.int32, device="cuda")[None].contiguous())
     eg = torch.from_numpy(tr.e[None].astype(np.int32)).cuda()
     go, glse = ks.ks_evict_attn_fwd(qa, ka, va, eg)
-    gdq, _, _ = ks.ks_evict_attn_bwd(qa, ka, va, eg, go, glse, da)
+    gdq, gdk, gdv = ks.ks_evict_attn_bwd(qa, ka, va, eg, go, glse, da)
     torch.cuda.synchronize()
     pos = np.arange(N)[None]
     q, k = O.rope(q, pos), O.rope(k, pos)
@@ -715,10 +972,12 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
         h = heads_used
         qh1, doh1 = q[:, :n, h:h + 1], do[:, :n, h:h + 1]
         ro, rl = O.attn_fwd(qh1, k[:, :n], v[:, :n], en)
-        rdq, _, _ = O.attn_bwd(qh1, k[:, :n], v[:, :n], en, doh1)
+        rdq, rdk, rdv = O.attn_bwd(qh1, k[:, :n], v[:, :n], en, doh1)
         done_pairs += pairs_n
         heads_used += 1
         ref.append((ro, rl, rdq))
+        rdk_sum = rdk if heads_used == 1 else rdk_sum + rdk
+        rdv_sum = rdv if heads_used == 1 else rdv_sum + rdv
     el = time.perf_counter() - t0
     # rows < n of the GPU's full-trace outputs against the oracle's prefix
     err = {"o": 0.0, "lse": 0.0, "dq": 0.0}
@@ -729,6 +988,15 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
             g = got.to("cpu", torch.float64).numpy()
             err[name] = max(err[name], float(np.abs(g - want).max()))
             scale_ref[name] = max(scale_ref[name], float(np.abs(want).max()))
+    # dK, dV of the keys whose every query lies inside the prefix (evicted by
+    # token n), summed over the kv group's query heads when all were timed
+    if heads_used == G:
+        done = np.flatnonzero(e[0, :n] <= n)
+        for name, got, want in (("dk", gdk[0, done, 0], rdk_sum[0, done, 0]),
+                                ("dv", gdv[0, done, 0], rdv_sum[0, done, 0])):
+            g = got.to("cpu", torch.float64).numpy()
+            err[name] = float(np.abs(g - want).max())
+            scale_ref[name] = float(np.abs(want).max())
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     model = "unknown"
     try:
@@ -748,8 +1016,10 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
         "sample": f"fp64 oracle forward + backward (dQ, dK, dV) of the first {n} tokens "
                   f"of trace 0, {heads_used} query head(s) of kv group 0: {done_pairs} live "
                   f"pairs in {el:.1f} s",
+        "_n": n, "_heads": heads_used, "_seconds": el,
         "gpu_vs_oracle_on_sample": {
             "rows": n, "heads": heads_used,
+            "keys_compared": int((e[0, :n] <= n).sum()) if heads_used == G else 0,
             "max_abs": {kk: round(vv, 6) for kk, vv in err.items()},
             "max_abs_of_reference": {kk: round(vv, 4) for kk, vv in scale_ref.items()},
         },

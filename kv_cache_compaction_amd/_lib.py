@@ -55,6 +55,9 @@ _SIGS = {
     "ks_paged_decode_rope": ([_vp] * 8 + [_i] * 8 + [_f, _f, _vp, _sz, _vp], _i),
     "ks_check_eviction_record": ([_vp, _i, _i, _vp, _vp], _i),
     "ks_check_block_table": ([_vp, _vp, _i, _i, _i, _i, _vp, _vp], _i),
+    # measurement aid (include/ks_measure.h)
+    "ks_measure_mfma_flops": ([_i, _i], ctypes.c_double),
+    "ks_measure_mfma_bf16": ([_vp, _vp, _i, _i, _vp], _i),
 }
 
 _lib = None
@@ -492,3 +495,18 @@ def ks_paged_decode_rope(q, pos, k_pool, v_pool, table, seq_lens, base=10000.0, 
     _check("ks_paged_decode_rope", st)
     return out, lse
 
+
+
+def ks_measure_mfma_flops(workgroups, iters):
+    return load_library().ks_measure_mfma_flops(workgroups, iters)
+
+
+def ks_measure_mfma_bf16(seed, sink, workgroups, iters, stream=None):
+    """Measurement aid: a loop of bf16 MFMAs only (include/ks_measure.h).
+    seed: >= 1024 bf16 values; sink: >= workgroups * 512 floats."""
+    lib = load_library()
+    _cuda_contig("seed", seed, torch.bfloat16)
+    _cuda_contig("sink", sink, torch.float32)
+    _need(seed.numel() >= 1024 and sink.numel() >= workgroups * 512, "seed/sink too small")
+    _check("ks_measure_mfma_bf16",
+           lib.ks_measure_mfma_bf16(_ptr(seed), _ptr(sink), workgroups, iters, _stream(stream)))
