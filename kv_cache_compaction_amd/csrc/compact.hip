@@ -455,28 +455,25 @@ __global__ __launch_bounds__(kThreads) void count_kept_kernel(
 // ---------------------------------------------------------------------------
 // Several events on rows longer than 4096 entries (token tables): the row
 // does not fit on chip, but which of its entries survive does.  Thread t
-// owns entries t + 1024 i (i < 64) and keeps one "alive" bit per entry.  Per
-// event, the rank of every alive entry in the current table is its position
-// in the (i, wave, lane) order among alive entries: wave ballots give counts
-// per (i, wave) cell, one workgroup scan over the 1024 cells gives their
-// offsets, and mbcnt the rank within the cell.  The event's keep flag of
-// that rank then decides the bit; each event's flag row is staged in LDS
-// while the previous event is processed.  After the last event the same
-// ranks are the output positions, and the table row is read once.
+// owns entries [64 t, 64 t + 64) of the original row as one 64-bit word of
+// survival bits.  The alive entries of a word sit at consecutive positions
+// [base, base + cnt) of the table an event applies to (base: a workgroup
+// scan of the per-word counts), so their keep flags are one 64-bit window
+// of the event's flags packed into bits in LDS; the window is deposited onto
+// the word's set bits (directly when it keeps or drops all of them, which
+// is every word away from an evicted run's ends).  kRowSplit workgroups per
+// row replay the events (one bit per entry: cheap) and each writes a
+// quarter of the compacted row, so the row's reads and writes spread over
+// four times as many compute units.
 // ---------------------------------------------------------------------------
 constexpr int kLongBits = 64;                        // entries per thread
 constexpr int kLongMax = kThreads * kLongBits;       // 65536 entries
+constexpr int kRowSplit = 4;                         // workgroups per row
 
-// Cell (i, w) is stored at cell[w * 64 + i] (a wave's cells contiguous) but
-// scanned in (i, w) order, the order of the entries t + 1024 i.
-__device__ __forceinline__ int cell_at(int i, int w) { return w * kLongBits + i; }
-
-// exclusive prefix over the cells in (i, w) order, in place; returns the
-// total (every thread)
-__device__ __forceinline__ int cell_scan(int* cell, int* wtot) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int at = cell_at(tid / kWaves, tid % kWaves);     // thread = cell in scan order
-  const int v = cell[at];
+// exclusive prefix of v over the workgroup's threads (in thread order); the
+// total goes to `total`.  Contains one barrier.
+__device__ __forceinline__ int block_scan(int v, int* wtot, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -492,143 +489,132 @@ __device__ __forceinline__ int cell_scan(int* cell, int* wtot) {
     off += i < w ? sw : 0;
     tot += sw;
   }
-  cell[at] = off + x - v;
-  __syncthreads();
-  return tot;
+  total = tot;
+  return off + x - v;
 }
 
-// counts of alive entries per (i, wave) cell
-// (lane i of each wave holds the count of its cell i)
-__device__ __forceinline__ void cell_counts(uint64_t alive, int* cell) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int mine = 0;
-  // partly unrolled on purpose: fully unrolled, the 64 loop-invariant lane
-  // compares are hoisted into scalar registers and spilled
-#pragma unroll 4
-  for (int i = 0; i < kLongBits; ++i) {
-    const int c = __popcll(__ballot((alive >> i) & 1));
-    mine = lane == i ? c : mine;
-  }
-  cell[cell_at(lane, w)] = mine;
-  __syncthreads();
-}
-
-// One event's keep row staged in LDS: the aligned 16-byte chunks that hold
-// the row's MB bytes (each chunk holds at least one byte of the row, so no
-// load leaves the pages the row lives on); byte k of the row is at
-// [delta + k].  Loads are issued into registers first (kStageRegs chunks
-// per thread) so that they fly while the previous event is processed.
-constexpr int kStageRegs = (kLongMax / 16 + 1 + kThreads - 1) / kThreads;   // 5
-constexpr int kStageBytes = (kLongMax / 16 + 1) * 16;   // chunks of one row, at most
-
-struct KeepStage {
-  u32x4 v[kStageRegs];
-  int delta;
-  int nchunk;
+// The 16-byte chunks that hold flags [64 t, 64 t + 64) of one keep row, read
+// at aligned addresses clamped to the chunks that hold bytes of the row (so
+// no load leaves the pages the row lives on).  Issued one event ahead.
+struct KeepChunks {
+  u32x4 c[5];
+  int shift;  // bytes from the first chunk to flag 64 t
 };
 
-__device__ __forceinline__ void stage_issue(const uint8_t* kr, int MB, KeepStage& st) {
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(kr);
-  const uintptr_t a0 = addr & ~static_cast<uintptr_t>(15);
-  st.delta = static_cast<int>(addr - a0);
-  st.nchunk = static_cast<int>((addr + MB - a0 + 15) >> 4);
-  const u32x4* src = reinterpret_cast<const u32x4*>(a0);
+__device__ __forceinline__ void keep_issue(const uint8_t* krow, int MB, int t, KeepChunks& k) {
+  const uintptr_t row = reinterpret_cast<uintptr_t>(krow);
+  const uintptr_t last = (row + static_cast<uintptr_t>(MB) - 1) & ~static_cast<uintptr_t>(15);
+  const uintptr_t a0 = (row + static_cast<uintptr_t>(64) * t) & ~static_cast<uintptr_t>(15);
+  k.shift = static_cast<int>(row + static_cast<uintptr_t>(64) * t - a0);
 #pragma unroll
-  for (int u = 0; u < kStageRegs; ++u) {
-    const int c = threadIdx.x + u * kThreads;
-    if (c < st.nchunk) st.v[u] = src[c];
+  for (int u = 0; u < 5; ++u) {
+    const uintptr_t a = a0 + 16 * u < last ? a0 + 16 * u : last;
+    k.c[u] = *reinterpret_cast<const u32x4*>(a);
   }
 }
 
-__device__ __forceinline__ void stage_store(const KeepStage& st, uint8_t* buf) {
+// four flag bytes -> four bits (bit i set iff byte i is nonzero)
+__device__ __forceinline__ uint32_t nz_nibble(uint32_t x) {
+  const uint32_t nz = (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
+  return ((nz >> 7) | (nz >> 14) | (nz >> 21) | (nz >> 28)) & 0xfu;
+}
+
+// flags [64 t, 64 t + 64) as bits; flags at or past `len` read as 0
+__device__ __forceinline__ uint64_t keep_bits(const KeepChunks& k, int t, int len) {
+  uint32_t w[3] = {0u, 0u, 0u};
 #pragma unroll
-  for (int u = 0; u < kStageRegs; ++u) {
-    const int c = threadIdx.x + u * kThreads;
-    if (c < st.nchunk) reinterpret_cast<u32x4*>(buf)[c] = st.v[u];
+  for (int i = 0; i < 20; ++i) w[i / 8] |= nz_nibble(k.c[i / 4][i % 4]) << (4 * (i % 8));
+  // bit offset = byte offset (one bit per flag byte)
+  const uint32_t lo = __builtin_amdgcn_alignbit(w[1], w[0], k.shift);
+  const uint32_t hi = __builtin_amdgcn_alignbit(w[2], w[1], k.shift);
+  uint64_t bits = (static_cast<uint64_t>(hi) << 32) | lo;
+  const int valid = len - 64 * t;
+  if (valid < 64) bits = valid <= 0 ? 0 : bits & ((uint64_t(1) << valid) - 1);
+  return bits;
+}
+
+__device__ __forceinline__ uint64_t low_bits(int n) {
+  return n >= 64 ? ~uint64_t(0) : (uint64_t(1) << n) - 1;
+}
+
+// bit i of `src` placed on the i-th set bit of `mask`
+__device__ __forceinline__ uint64_t deposit(uint64_t src, uint64_t mask) {
+  uint64_t out = 0;
+  while (mask) {
+    const uint64_t low = mask & (~mask + 1);
+    if (src & 1) out |= low;
+    src >>= 1;
+    mask &= mask - 1;
   }
+  return out;
 }
 
 __global__ __launch_bounds__(kThreads) void compact_rounds_long_kernel(
     const int32_t* __restrict__ tin, const int32_t* __restrict__ nin,
     const uint8_t* __restrict__ keep, int rounds, int32_t* __restrict__ tout,
     int32_t* __restrict__ nout, const int32_t* __restrict__ pin,
-    int32_t* __restrict__ pout, int B, int MB) {
-  __shared__ __attribute__((aligned(16))) int cell[kThreads];
+    int32_t* __restrict__ pout, int B, int MB, int split) {
+  __shared__ uint64_t kbits[kThreads + 1];   // one event's flags, by table position
+  __shared__ uint64_t fword[kThreads];       // survival words after the last event
+  __shared__ int fbase[kThreads];            // output position of each word's first entry
   __shared__ int wtot[kWaves];
-  __shared__ __attribute__((aligned(16))) uint8_t kst[2][kStageBytes];
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int b = blockIdx.x / split, part = blockIdx.x % split;
+  const int tid = threadIdx.x;
   const size_t row = static_cast<size_t>(b) * MB;
   const size_t rstride = static_cast<size_t>(B) * MB;
   int n = nin[b];
   n = n < 0 ? 0 : (n > MB ? MB : n);
-  uint64_t alive = 0;
-#pragma unroll
-  for (int i = 0; i < kLongBits; ++i)
-    alive |= static_cast<uint64_t>(tid + kThreads * i < n) << i;
+  const int e0 = 64 * tid;
+  uint64_t word = e0 >= n ? 0 : low_bits(n - e0);
+  if (tid == 0) kbits[kThreads] = 0;
 
-  KeepStage st;
-  if (rounds > 0) {
-    stage_issue(keep + row, MB, st);
-    stage_store(st, kst[0]);
-  }
+  KeepChunks kc;
+  if (rounds > 0) keep_issue(keep + row, MB, tid, kc);
   for (int r = 0; r < rounds; ++r) {
-    const int delta = st.delta;
-    const uint8_t* kl = kst[r & 1] + delta;
-    // next event's flags: in flight while this one is processed
-    if (r + 1 < rounds) stage_issue(keep + (r + 1) * rstride + row, MB, st);
-    cell_counts(alive, cell);      // its barrier also publishes kst[r & 1]
-    cell_scan(cell, wtot);
-    // branch-free: every lane reads a flag (a lane that is not alive reads
-    // byte <= the event's length, inside the staged row) and masks it
-    uint64_t next = 0;
-#pragma unroll 1
-    for (int i0 = 0; i0 < kLongBits; i0 += 16) {
-      int rk[16];
-      const int4* cw = reinterpret_cast<const int4*>(cell + cell_at(i0, w));
-      const int4 c4[4] = {cw[0], cw[1], cw[2], cw[3]};
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint64_t m = __ballot((alive >> (i0 + j)) & 1);
-        const int4 c = c4[j / 4];
-        const int cj = (j % 4 == 0) ? c.x : (j % 4 == 1) ? c.y : (j % 4 == 2) ? c.z : c.w;
-        rk[j] = cj + lane_rank(m);
-      }
-      int fl[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) fl[j] = kl[rk[j]];
-      // keep the 16 gathers in flight together (left alone, the scheduler
-      // waits for each one before issuing the next)
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint64_t f = fl[j] != 0;
-        next |= (f & (alive >> (i0 + j))) << (i0 + j);
-      }
+    const int cnt = __popcll(word);
+    int len;  // entries of the table this event applies to
+    const int base = block_scan(cnt, wtot, len);
+    // the event's flags as bits (only positions inside that table are ever
+    // consulted: every window below lies in [0, len))
+    if (64 * tid < len) kbits[tid] = keep_bits(kc, tid, MB);
+    // the next event's flags: in flight while this one is applied
+    if (r + 1 < rounds) keep_issue(keep + (r + 1) * rstride + row, MB, tid, kc);
+    __syncthreads();
+    if (cnt) {
+      const int q = base >> 6, sh = base & 63;
+      uint64_t km = kbits[q] >> sh;
+      if (sh) km |= kbits[q + 1] << (64 - sh);
+      km &= low_bits(cnt);
+      if (km == 0)
+        word = 0;
+      else if (km != low_bits(cnt))
+        word = deposit(km, word);
     }
-    alive = next;
-    if (r + 1 < rounds) stage_store(st, kst[(r + 1) & 1]);
-    __syncthreads();  // cell is rewritten by the next event
+    __syncthreads();  // kbits is rewritten by the next event
   }
 
-  cell_counts(alive, cell);
-  const int total = cell_scan(cell, wtot);
-  // 16 entries per batch: loads (clamped into the row) all in flight, then
-  // the stores of the alive ones
+  int total;
+  const int base = block_scan(__popcll(word), wtot, total);
+  fword[tid] = word;
+  fbase[tid] = base;
+  __syncthreads();
+  // this workgroup's share of the row: entries [e_lo, e_hi), 16 per thread
+  // per pass, loads (clamped into the row) all in flight before the stores
+  const int words = (MB + kLongBits - 1) / kLongBits;
+  const int sw = (words + split - 1) / split;
+  const int e_lo = part * sw * kLongBits, e_hi = min(MB, e_lo + sw * kLongBits);
 #pragma unroll 1
-  for (int i0 = 0; i0 < kLongBits; i0 += 16) {
+  for (int c0 = e_lo; c0 < e_hi; c0 += 16 * kThreads) {
     int dst[16], v[16], pv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const bool a = (alive >> (i0 + j)) & 1;
-      const uint64_t m = __ballot(a);
-      dst[j] = a ? cell[cell_at(i0 + j, w)] + lane_rank(m) : -1;
-      const size_t src = row + min(tid + kThreads * (i0 + j), MB - 1);
-      v[j] = tin[src];
-      pv[j] = pin ? pin[src] : 0;
+      const int e = c0 + tid + kThreads * j;
+      const int ec = min(e, MB - 1);
+      const uint64_t fw = e < e_hi ? fword[ec >> 6] : 0;
+      const int bit = ec & 63;
+      dst[j] = (fw >> bit) & 1 ? fbase[ec >> 6] + __popcll(fw & ((uint64_t(1) << bit) - 1)) : -1;
+      v[j] = tin[row + ec];
+      pv[j] = pin ? pin[row + ec] : 0;
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -638,11 +624,15 @@ __global__ __launch_bounds__(kThreads) void compact_rounds_long_kernel(
       }
     }
   }
-  for (int k = total + tid; k < MB; k += kThreads) {
+  // the tail [total, MB) is -1, split between the row's workgroups
+  const int tail = MB - total;
+  const int per = (tail + split - 1) / split;
+  const int t0 = total + part * per, t1 = min(MB, t0 + per);
+  for (int k = t0 + tid; k < t1; k += kThreads) {
     tout[row + k] = -1;
     if (pout) pout[row + k] = -1;
   }
-  if (tid == 0) nout[b] = total;
+  if (part == 0 && tid == 0) nout[b] = total;
 }
 
 }  // namespace
@@ -744,9 +734,15 @@ extern "C" ks_status ks_compact_block_table_rounds(const int32_t* table_in,
     hipLaunchKernelGGL(compact_rounds_kernel, dim3(B), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), table_in, nblk_in, keep, rounds,
                        table_out, nblk_out, pos_in, pos_out, B, max_blocks);
-  else
-    hipLaunchKernelGGL(compact_rounds_long_kernel, dim3(B), dim3(kThreads), 0,
+  else {
+    // several workgroups per row, unless the lengths are updated in place
+    // (every workgroup reads nblk_in; only one may then exist per row)
+    const int split = nblk_in == nblk_out ? 1 : kRowSplit;
+    KS_REQUIRE(static_cast<int64_t>(B) * split < (int64_t{1} << 31),
+               "ks_compact_block_table_rounds: grid too large");
+    hipLaunchKernelGGL(compact_rounds_long_kernel, dim3(B * split), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), table_in, nblk_in, keep, rounds,
-                       table_out, nblk_out, pos_in, pos_out, B, max_blocks);
+                       table_out, nblk_out, pos_in, pos_out, B, max_blocks, split);
+  }
   return ks_check_launch("ks_compact_block_table_rounds");
 }
