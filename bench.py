@@ -409,6 +409,8 @@ def main():
     for p in parts.values():
         if p["bound"] == "mfma":
             p["frac_of_measured"] = round(p["achieved"] / mfma["tflops"], 4)
+    result["fused_dq_atomics_probe"] = dq_atomics_probe(ks, torch, stream, e_np, trn,
+                                                      ms["attn_bwd"])
     result["hbm_reference"] = hbm_reference(torch, stream)
     result["single_token_blocks"] = token_granular_decode(ks, torch, stream, dec)
     result["toy_stack"] = toy_stack_mismatch(torch)
@@ -714,6 +716,33 @@ def mfma_rate(ks, torch, stream, workgroups=2048, iters=2500):
             "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
             "frac_of_published_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                             4)}
+
+
+def dq_atomics_probe(ks, torch, stream, e_np, cfg, bwd_ms, reps=3):
+    """The dQ adds a single-pass backward would issue from the dK/dV walk on
+    the same traces (every 256-key workgroup adding a 32 x 128 fp32 partial
+    per query chunk and head, global fp32 atomics), timed alone: the case
+    against fusing dQ into the dK/dV kernel."""
+    B, N, Hq, Hkv = cfg.batch, cfg.N, cfg.Hq, cfg.Hkv
+    G = Hq // Hkv
+    nkt = (N + 255) // 256
+    cend = np.zeros((B, nkt), np.int32)
+    for b in range(B):
+        em = np.maximum.reduceat(e_np[b].astype(np.int64), np.arange(0, N, 256))
+        cend[b] = (np.minimum(N, em) + 31) // 32
+    units = int(sum(max(0, int(cend[b, t]) - 8 * t) for b in range(B) for t in range(nkt))) * G * Hkv
+    acc = torch.zeros((B, N, Hq, 128), dtype=torch.float32, device="cuda")
+    cg = torch.from_numpy(cend).cuda()
+    run = lambda: ks.ks_measure_dq_atomics(acc, cg, Hkv, stream=stream)
+    ms = _median_ms(torch, stream, run, reps)
+    nbytes = units * 32 * 128 * 4
+    del acc
+    torch.cuda.empty_cache()
+    return {"what": "fp32 atomic dQ adds of a dK/dV-walk backward (256-key workgroups, "
+                    "32-row chunks), nothing else", "chunk_head_units": units,
+            "atomic_bytes": nbytes, "ms": round(ms, 3),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "backward_ms_two_kernels": round(bwd_ms, 3)}
 
 
 def _median_ms(torch, stream, fn, reps):

@@ -13,5 +13,5 @@ from ._lib import (  # noqa: F401
     ks_append_kv_bs1, ks_check_block_table, ks_check_eviction_record, ks_paged_decode, ks_paged_decode_bs1, ks_paged_decode_bs1_workspace,
     ks_paged_decode_noalloc, ks_paged_decode_noalloc_max_scratch, ks_paged_decode_rope,
     ks_paged_decode_workspace, ks_rope_logical, load_library, ks_measure_mfma_bf16,
-    ks_measure_mfma_flops,
+    ks_measure_mfma_flops, ks_measure_dq_atomics,
 )

@@ -58,6 +58,7 @@ _SIGS = {
     # measurement aid (include/ks_measure.h)
     "ks_measure_mfma_flops": ([_i, _i], ctypes.c_double),
     "ks_measure_mfma_bf16": ([_vp, _vp, _i, _i, _vp], _i),
+    "ks_measure_dq_atomics": ([_vp, _vp, _i, _i, _i, _i, _vp], _i),
 }
 
 _lib = None
@@ -510,3 +511,17 @@ def ks_measure_mfma_bf16(seed, sink, workgroups, iters, stream=None):
     _need(seed.numel() >= 1024 and sink.numel() >= workgroups * 512, "seed/sink too small")
     _check("ks_measure_mfma_bf16",
            lib.ks_measure_mfma_bf16(_ptr(seed), _ptr(sink), workgroups, iters, _stream(stream)))
+
+
+def ks_measure_dq_atomics(acc, cend, Hkv, stream=None):
+    """Measurement aid: the fp32 atomic dQ adds of a single-pass backward
+    (include/ks_measure.h).  acc: fp32 [B, N, Hq, 128]; cend: int32
+    [B, ceil(N / 256)]."""
+    lib = load_library()
+    B, N, Hq, Dd = acc.shape
+    _need(Dd == 128 and Hq % Hkv == 0, "acc must be [B, N, Hq, 128]")
+    _cuda_contig("acc", acc, torch.float32)
+    _cuda_contig("cend", cend, torch.int32)
+    _need(tuple(cend.shape) == (B, (N + 255) // 256), "cend shape")
+    _check("ks_measure_dq_atomics",
+           lib.ks_measure_dq_atomics(_ptr(acc), _ptr(cend), B, N, Hq, Hkv, _stream(stream)))

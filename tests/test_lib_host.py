@@ -18,7 +18,10 @@ def lib():
 
 
 def test_exports_every_declared_symbol(lib):
-    names = ks.header_functions()
+    import glob
+    import os
+    names = sorted({n for h in glob.glob(os.path.join(os.path.dirname(ks._lib.HEADER), "*.h"))
+                    for n in ks.header_functions(h)})
     assert {"ks_rope_logical", "ks_evict_attn_fwd", "ks_evict_attn_bwd",
             "ks_compact_block_table", "ks_paged_decode", "ks_last_error"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ks.LIB_PATH], capture_output=True,
@@ -164,9 +167,13 @@ def test_fused_rope_decode_argument_checks(lib):
 def test_binding_signatures_match_header():
     """Every function the binding describes has the header's parameter count
     (a wrong count would pass garbage through ctypes without an error)."""
+    import glob
+    import os
     import re
-    text = re.sub(r"/\*.*?\*/", "", open(ks._lib.HEADER).read(), flags=re.S)
-    decls = dict(re.findall(r"\b(ks_[a-z0-9_]+)\s*\(([^;{]*)\)\s*;", text))
+    decls = {}
+    for h in glob.glob(os.path.join(os.path.dirname(ks._lib.HEADER), "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        decls.update(re.findall(r"\b(ks_[a-z0-9_]+)\s*\(([^;{]*)\)\s*;", text))
     for name, (args, _) in _lib._SIGS.items():
         assert name in decls, name
         params = decls[name].strip()
