@@ -558,7 +558,9 @@ __global__ __launch_bounds__(kThreads) void compact_rounds_long_kernel(
   __shared__ uint64_t fword[kThreads];       // survival words after the last event
   __shared__ int fbase[kThreads];            // output position of each word's first entry
   __shared__ int wtot[kWaves];
-  const int b = blockIdx.x / split, part = blockIdx.x % split;
+  // the row's workgroups are B apart in the grid, so with B a multiple of 8
+  // they run on one XCD and its L2 serves the keep rows they all read
+  const int b = blockIdx.x % B, part = blockIdx.x / B;
   const int tid = threadIdx.x;
   const size_t row = static_cast<size_t>(b) * MB;
   const size_t rstride = static_cast<size_t>(B) * MB;
