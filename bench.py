@@ -106,8 +106,9 @@ def executed_flops(e: np.ndarray, Hq: int, Hkv: int, D: int, kt: int = 64):
 # HIP sources each entry point's kernels are built from (a stored counter
 # summary applies only to the kernels it was taken on)
 ENTRY_SOURCES = {
-    "ks_evict_attn_fwd": ("ks_common.h", "attn_common.h", "attn_fwd.hip"),
-    "ks_evict_attn_bwd": ("ks_common.h", "attn_common.h", "attn_fwd.hip", "attn_bwd.hip"),
+    "ks_evict_attn_fwd_rope": ("ks_common.h", "attn_common.h", "attn_fwd.hip", "rope.hip"),
+    "ks_evict_attn_bwd_rope": ("ks_common.h", "attn_common.h", "attn_fwd.hip", "attn_bwd.hip",
+                               "rope.hip"),
     "ks_paged_decode": ("ks_common.h", "decode.hip"),
     "ks_paged_decode_bs1": ("ks_common.h", "decode.hip"),
     "ks_compact_block_table_rounds": ("ks_common.h", "compact.hip"),
@@ -202,16 +203,17 @@ def main():
     do = normal_tensor((B, N, Hq, D), seeds["do"], trn.value_scale, bf, dev)
     e = torch.from_numpy(e_np).to(dev)
     pos = torch.arange(N, dtype=torch.int32, device=dev)[None].repeat(B, 1).contiguous()
-    # every step rotates fresh copies of the raw projections (ks_rope_logical
-    # works in place), so the timed attention always runs on the inputs the
-    # tests check; the copies are made outside the timed stages
-    q_raw, k_raw = q.clone(), k.clone()
+    # q and k are the raw projections: the attention entry points rotate
+    # them at their logical positions (k once into k_rot, q in the forward
+    # kernel, which stores q_rot for the backward) and leave them unchanged
+    q_rot, k_rot = torch.empty_like(q), torch.empty_like(k)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_f = torch.empty(ks.ks_evict_attn_fwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+    lib = ks.load_library()
+    ws_f = torch.empty(lib.ks_evict_attn_fwd_rope_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
                        dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(ks.ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+    ws_b = torch.empty(lib.ks_evict_attn_bwd_rope_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
                        dtype=torch.uint8, device=dev)
     pairs = live_pairs(e_np)
     ex_fwd, ex_dq, ex_dkdv = executed_flops(e_np, Hq, Hkv, D)
@@ -264,16 +266,13 @@ def main():
         def t1(ev, name):
             if tm:
                 tm.stop(ev, name)
-        q.copy_(q_raw)
-        k.copy_(k_raw)
         ev = t0()
-        ks.ks_rope_logical(q, k, pos, stream=stream)
-        t1(ev, "rope")
-        ev = t0()
-        ks.ks_evict_attn_fwd(q, k, v, e, out=o, lse=lse, ws=ws_f, stream=stream)
+        ks.ks_evict_attn_fwd_rope(q, k, v, e, pos, q_rot=q_rot, k_rot=k_rot, out=o, lse=lse,
+                                  ws=ws_f, stream=stream)
         t1(ev, "attn_fwd")
         ev = t0()
-        ks.ks_evict_attn_bwd(q, k, v, e, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws_b, stream=stream)
+        ks.ks_evict_attn_bwd_rope(q_rot, k_rot, v, e, pos, o, lse, do, dq=dq, dk=dk, dv=dv,
+                                  ws=ws_b, stream=stream)
         t1(ev, "attn_bwd")
         ev = t0()
         # the step's compaction events, applied together in one launch
@@ -351,9 +350,6 @@ def main():
                     "achieved": comp_bytes / (ms["compact"] * 1e-3) / 1e9, "unit": "GB/s"},
         "compact_2^26": {"bound": "hbm", "ms": scan_ms,
                          "achieved": scan_bytes / (scan_ms * 1e-3) / 1e9, "unit": "GB/s"},
-        "rope": {"bound": "hbm", "ms": ms["rope"],
-                 "achieved": 2 * (q.numel() + k.numel()) * 2 / (ms["rope"] * 1e-3) / 1e9,
-                 "unit": "GB/s"},
     }
     for p in parts.values():
         peak = MFMA_BF16_PEAK_TFLOPS if p["bound"] == "mfma" else HBM_PEAK_GBS
@@ -390,14 +386,14 @@ def main():
         "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "stage_ms": {kk: round(vv, 4) for kk, vv in ms.items()},
         "roofline": {
-            "kernel": f"ks_{'evict_attn_bwd' if dom == 'attn_bwd' else 'evict_attn_fwd'}",
+            "kernel": f"ks_{'evict_attn_bwd' if dom == 'attn_bwd' else 'evict_attn_fwd'}_rope",
             "bound": "mfma",
             "achieved": round(parts[dom]["achieved"], 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(parts[dom]["frac"], 4),
             "traffic": stored_traffic(
-                f"ks_{'evict_attn_bwd' if dom == 'attn_bwd' else 'evict_attn_fwd'}"),
+                f"ks_{'evict_attn_bwd' if dom == 'attn_bwd' else 'evict_attn_fwd'}_rope"),
         },
         "stages": {kk: {x: (round(y, 4) if isinstance(y, float) else y) for x, y in vv.items()}
                    for kk, vv in parts.items()},
@@ -423,7 +419,7 @@ def main():
         dec_gpu = dict(db=db, kp=kp, vp=vp, q=q4[:, 0], k_new=k4, v_new=v4, pos=db.pos,
                        out=out4, lse=lse4, table=tbufs[0], ms=ms["compact"] + ms["decode"])
         result["cpu_baseline"]["per_config"] = cpu_per_config(
-            small, result["cpu_baseline"], traces, trn, ms["rope"] + attn_ms, dec_gpu,
+            small, result["cpu_baseline"], traces, trn, attn_ms, dec_gpu,
             result["long_mixed_64k"])
         for key in ("_n", "_heads", "_seconds"):
             result["cpu_baseline"].pop(key)
@@ -586,15 +582,21 @@ def reprefill_counterfactual(ks, torch, traces, q, k, v, do, stream, ms, pairs, 
     op = torch.empty_like(qp)
     lsep = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     dqp, dkp, dvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
-    wsf = torch.empty(ks.ks_evict_attn_fwd_workspace(B, L, Hq, Hkv, D, ks.KS_BF16),
+    # the same fused entry points as the step; kept tokens keep their
+    # original (logical) positions in every segment
+    posp = idx.to(torch.int32).contiguous()
+    qr, kr = torch.empty_like(qp), torch.empty_like(kp)
+    lib = ks.load_library()
+    wsf = torch.empty(lib.ks_evict_attn_fwd_rope_workspace(B, L, Hq, Hkv, D, ks.KS_BF16),
                       dtype=torch.uint8, device=dev)
-    wsb = torch.empty(ks.ks_evict_attn_bwd_workspace(B, L, Hq, Hkv, D, ks.KS_BF16),
+    wsb = torch.empty(lib.ks_evict_attn_bwd_rope_workspace(B, L, Hq, Hkv, D, ks.KS_BF16),
                       dtype=torch.uint8, device=dev)
 
     def run():
-        ks.ks_evict_attn_fwd(qp, kp, vp, ep, out=op, lse=lsep, ws=wsf, stream=stream)
-        ks.ks_evict_attn_bwd(qp, kp, vp, ep, op, lsep, dop, dq=dqp, dk=dkp, dv=dvp, ws=wsb,
-                             stream=stream)
+        ks.ks_evict_attn_fwd_rope(qp, kp, vp, ep, posp, q_rot=qr, k_rot=kr, out=op, lse=lsep,
+                                  ws=wsf, stream=stream)
+        ks.ks_evict_attn_bwd_rope(qr, kr, vp, ep, posp, op, lsep, dop, dq=dqp, dk=dkp, dv=dvp,
+                                  ws=wsb, stream=stream)
     run()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -629,7 +631,7 @@ def long_mixed_64k(ks, torch, stream, reps=5):
     compacted by sliding window, prompt+recent and summary in turn, 64 q /
     8 kv heads, D = 128.  Median over reps of each pass, timed with HIP
     events on the library's stream; useful TFLOP/s with the step's
-    convention (RoPE applied once beforehand, not timed)."""
+    convention (RoPE fused into the timed forward and backward)."""
     from workloads import LONG_MIXED_64K, config_trace_batch, normal_tensor, stacked_e
 
     cfg = LONG_MIXED_64K
@@ -643,17 +645,19 @@ def long_mixed_64k(ks, torch, stream, reps=5):
     do = normal_tensor((B, N, Hq, D), seeds["do"], cfg.value_scale, bf, dev)
     e = torch.from_numpy(e_np).to(dev)
     pos = torch.arange(N, dtype=torch.int32, device=dev)[None].repeat(B, 1).contiguous()
-    ks.ks_rope_logical(q, k, pos, stream=stream)
+    q_rot, k_rot = torch.empty_like(q), torch.empty_like(k)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    wsf = torch.empty(ks.ks_evict_attn_fwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+    lib = ks.load_library()
+    wsf = torch.empty(lib.ks_evict_attn_fwd_rope_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
                       dtype=torch.uint8, device=dev)
-    wsb = torch.empty(ks.ks_evict_attn_bwd_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
+    wsb = torch.empty(lib.ks_evict_attn_bwd_rope_workspace(B, N, Hq, Hkv, D, ks.KS_BF16),
                       dtype=torch.uint8, device=dev)
-    fwd = lambda: ks.ks_evict_attn_fwd(q, k, v, e, out=o, lse=lse, ws=wsf, stream=stream)
-    bwd = lambda: ks.ks_evict_attn_bwd(q, k, v, e, o, lse, do, dq=dq, dk=dk, dv=dv, ws=wsb,
-                                       stream=stream)
+    fwd = lambda: ks.ks_evict_attn_fwd_rope(q, k, v, e, pos, q_rot=q_rot, k_rot=k_rot, out=o,
+                                            lse=lse, ws=wsf, stream=stream)
+    bwd = lambda: ks.ks_evict_attn_bwd_rope(q_rot, k_rot, v, e, pos, o, lse, do, dq=dq, dk=dk,
+                                            dv=dv, ws=wsb, stream=stream)
     fwd()
     bwd()
     torch.cuda.synchronize()
@@ -687,7 +691,7 @@ def long_mixed_64k(ks, torch, stream, reps=5):
         "bwd_tflops_useful": round(useful_b / (mb * 1e-3) / 1e12, 2),
         "executed_over_useful": round((ex_f + ex_q + ex_kv) / (useful_f + useful_b), 4),
     }
-    del q, k, v, do, o, dq, dk, dv, wsf, wsb
+    del q, k, v, do, o, dq, dk, dv, wsf, wsb, q_rot, k_rot
     torch.cuda.empty_cache()
     return out
 
@@ -785,13 +789,13 @@ def small_configs_gpu(ks, torch, stream, reps=20):
         dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(g["v"])
         rec = {"cfg": cfg, "traces": traces, "raw": raw}
         if cfg.backward:
+            # the step's fused entry points (qg, kg receive the rotated q, k;
+            # dq, dk are gradients of the unrotated projections)
             def run():
-                qg.copy_(g["q"])
-                kg.copy_(g["k"])
-                ks.ks_rope_logical(qg, kg, pos, stream=stream)
-                ks.ks_evict_attn_fwd(qg, kg, g["v"], e, out=o, lse=lse, stream=stream)
-                ks.ks_evict_attn_bwd(qg, kg, g["v"], e, o, lse, g["do"], dq=dq, dk=dk, dv=dv,
-                                     stream=stream)
+                ks.ks_evict_attn_fwd_rope(g["q"], g["k"], g["v"], e, pos, q_rot=qg, k_rot=kg,
+                                          out=o, lse=lse, stream=stream)
+                ks.ks_evict_attn_bwd_rope(qg, kg, g["v"], e, pos, o, lse, g["do"], dq=dq, dk=dk,
+                                          dv=dv, stream=stream)
         else:
             perm = np.random.default_rng(7).permutation(32).astype(np.int32)[None]
             keep = trace_blocks_keep(traces[0])[None]
@@ -869,6 +873,8 @@ def cpu_per_config(small, base, traces, cfg3, gpu3_ms, dec, mixed):
     ro, rl = O.attn_fwd(qr, kr, vv, e)
     rdq, rdk, rdv = O.attn_bwd(qr, kr, vv, e, dd)
     el = time.perf_counter() - t0
+    # the GPU's dq, dk are gradients of the unrotated projections
+    rdq, rdk = O.rope(rdq, pos, inverse=True), O.rope(rdk, pos, inverse=True)
     err = {nm: float(np.abs(f64(r[nm]) - ref).max())
            for nm, ref in (("o", ro), ("lse", rl), ("dq", rdq), ("dk", rdk), ("dv", rdv))}
     res["train-4k"] = {"work": "RoPE + masked forward + backward, 4096 tokens, 8 q / 2 kv heads",
@@ -981,10 +987,11 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
     # the GPU path on the same trace (whole trace, every head), for the error
     # of the sampled rows against the oracle
     import kv_cache_compaction_amd as ks
-    ks.ks_rope_logical(qa, ka, torch.arange(N, dtype=torch.int32, device="cuda")[None].contiguous())
     eg = torch.from_numpy(tr.e[None].astype(np.int32)).cuda()
-    go, glse = ks.ks_evict_attn_fwd(qa, ka, va, eg)
-    gdq, gdk, gdv = ks.ks_evict_attn_bwd(qa, ka, va, eg, go, glse, da)
+    pg = torch.arange(N, dtype=torch.int32, device="cuda")[None].contiguous()
+    go, glse, qrg, krg = ks.ks_evict_attn_fwd_rope(qa, ka, va, eg, pg)
+    gdq, gdk, gdv = ks.ks_evict_attn_bwd_rope(qrg, krg, va, eg, pg, go, glse, da)
+    del qrg, krg
     torch.cuda.synchronize()
     pos = np.arange(N)[None]
     q, k = O.rope(q, pos), O.rope(k, pos)
@@ -1008,7 +1015,12 @@ def cpu_baseline(traces, seeds, cfg, budget_s):
         rdk_sum = rdk if heads_used == 1 else rdk_sum + rdk
         rdv_sum = rdv if heads_used == 1 else rdv_sum + rdv
     el = time.perf_counter() - t0
-    # rows < n of the GPU's full-trace outputs against the oracle's prefix
+    # rows < n of the GPU's full-trace outputs against the oracle's prefix;
+    # the GPU's dq, dk are gradients of the unrotated projections
+    unrot = lambda x: O.rope(x, pos[:, :n], inverse=True)
+    ref = [(ro, rl, unrot(rdq)) for ro, rl, rdq in ref]
+    if heads_used == G:
+        rdk_sum = unrot(rdk_sum)
     err = {"o": 0.0, "lse": 0.0, "dq": 0.0}
     scale_ref = {"o": 0.0, "lse": 0.0, "dq": 0.0}
     for h, (ro, rl, rdq) in enumerate(ref):

@@ -154,6 +154,62 @@ ks_status ks_evict_attn_bwd(const void* q, const void* k, const void* v,
                             void* stream);
 
 /*
+ * ks_evict_attn_fwd_rope -- ks_rope_logical and ks_evict_attn_fwd in one
+ * call, for the training step.
+ *
+ * Queries and keys arrive UNROTATED; every token is rotated at its logical
+ * position pos (explainer, the RoPE paragraph; same angles and rounding as
+ * ks_rope_logical, so q_rot, k_rot, o and lse are bit-identical to
+ * ks_rope_logical followed by ks_evict_attn_fwd).  The keys are rotated
+ * once, out of place, into k_rot; each query row is rotated in registers by
+ * the attention kernel, which also stores it to q_rot.  q and k are not
+ * modified.  q_rot and k_rot are what ks_evict_attn_bwd_rope takes.
+ *
+ * q      [B, N, Hq, D] unrotated queries;  k, v [B, N, Hkv, D]
+ * e      int32 [B, N] as in ks_evict_attn_fwd; pos int32 [B, N] (device)
+ * q_rot  [B, N, Hq, D], k_rot [B, N, Hkv, D] outputs; must not overlap q, k
+ * o, lse outputs as in ks_evict_attn_fwd (lse required)
+ * dtype  KS_BF16 with D = 128 (else KS_ERR_UNSUPPORTED); base > 1.
+ * ws     workspace of at least ks_evict_attn_fwd_rope_workspace() bytes
+ *        (the tile summary and a [B*N][D/2] (cos, sin) table).
+ */
+size_t ks_evict_attn_fwd_rope_workspace(int B, int N, int Hq, int Hkv, int D,
+                                        int dtype);
+ks_status ks_evict_attn_fwd_rope(const void* q, const void* k, const void* v,
+                                 const int32_t* e, const int32_t* pos,
+                                 void* q_rot, void* k_rot, void* o, float* lse,
+                                 int B, int N, int Hq, int Hkv, int D,
+                                 int dtype, float scale, float base, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
+ * ks_evict_attn_bwd_rope -- gradients of ks_evict_attn_fwd_rope with
+ * respect to the UNROTATED q and k (and v).
+ *
+ * The softmax backward of ks_evict_attn_bwd on the rotated operands; dQ and
+ * dK are then rotated by -theta in fp32 before their single rounding to
+ * bf16 (the rotation is orthogonal, so its backward is its transpose).  This
+ * replaces ks_evict_attn_bwd followed by ks_rope_logical(inverse=1) and
+ * skips that second rounding, so dq and dk agree with it to one bf16 ulp,
+ * not bit for bit; dv is bit-identical.
+ *
+ * q_rot, k_rot  the rotated operands written by ks_evict_attn_fwd_rope
+ * pos, base     the logical positions and base given to the forward
+ * other arguments as in ks_evict_attn_bwd; dtype KS_BF16 with D = 128.
+ * ws            at least ks_evict_attn_bwd_rope_workspace() bytes.
+ */
+size_t ks_evict_attn_bwd_rope_workspace(int B, int N, int Hq, int Hkv, int D,
+                                        int dtype);
+ks_status ks_evict_attn_bwd_rope(const void* q_rot, const void* k_rot,
+                                 const void* v, const int32_t* e,
+                                 const int32_t* pos, const void* o,
+                                 const float* lse, const void* dout, void* dq,
+                                 void* dk, void* dv, int B, int N, int Hq,
+                                 int Hkv, int D, int dtype, float scale,
+                                 float base, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
  * ks_compact_block_table -- splice evicted blocks out of paged block tables.
  *
  * The table may not keep empty slots, so complete blocks are removed and the

@@ -42,6 +42,10 @@ _SIGS = {
                            _vp], _i),
     "ks_evict_attn_bwd_workspace": ([_i, _i, _i, _i, _i, _i], _sz),
     "ks_evict_attn_bwd": ([_vp] * 10 + [_i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+    "ks_evict_attn_fwd_rope_workspace": ([_i, _i, _i, _i, _i, _i], _sz),
+    "ks_evict_attn_fwd_rope": ([_vp] * 9 + [_i, _i, _i, _i, _i, _i, _f, _f, _vp, _sz, _vp], _i),
+    "ks_evict_attn_bwd_rope_workspace": ([_i, _i, _i, _i, _i, _i], _sz),
+    "ks_evict_attn_bwd_rope": ([_vp] * 11 + [_i, _i, _i, _i, _i, _i, _f, _f, _vp, _sz, _vp], _i),
     "ks_compact_block_table": ([_vp] * 7 + [_i, _i, _vp], _i),
     "ks_compact_block_table_rounds": ([_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp], _i),
     "ks_paged_decode_workspace": ([_i, _i, _i, _i], _sz),
@@ -220,6 +224,70 @@ def ks_evict_attn_bwd(q, k, v, e, o, lse, dout, scale=None, dq=None, dk=None, dv
                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, N, Hq, Hkv, D, code,
                                sc, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("ks_evict_attn_bwd", st)
+    return dq, dk, dv
+
+
+def ks_evict_attn_fwd_rope(q, k, v, e, pos, base=10000.0, scale=None, q_rot=None, k_rot=None,
+                           out=None, lse=None, ws=None, stream=None):
+    """RoPE at logical positions fused into the masked forward; q and k are
+    unrotated and left unchanged.  Returns (o, lse, q_rot, k_rot)."""
+    lib = load_library()
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _cuda_contig("q", q)
+    _cuda_contig("k", k, q.dtype)
+    _cuda_contig("v", v, q.dtype)
+    _cuda_contig("e", e, torch.int32)
+    _cuda_contig("pos", pos, torch.int32)
+    _need(tuple(k.shape) == (B, N, Hkv, D) and tuple(v.shape) == (B, N, Hkv, D), "k/v shape")
+    _need(tuple(e.shape) == (B, N) and tuple(pos.shape) == (B, N), "e/pos must be [B, N]")
+    q_rot = torch.empty_like(q) if q_rot is None else _given("q_rot", q_rot, q.shape, q.dtype)
+    k_rot = torch.empty_like(k) if k_rot is None else _given("k_rot", k_rot, k.shape, q.dtype)
+    out = torch.empty_like(q) if out is None else _given("out", out, q.shape, q.dtype)
+    lse = (torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None
+           else _given("lse", lse, (B, Hq, N), torch.float32))
+    code = _dtype_code(q)
+    nbytes = lib.ks_evict_attn_fwd_rope_workspace(B, N, Hq, Hkv, D, code)
+    ws = _workspace(nbytes, q.device, ws)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.ks_evict_attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(e), _ptr(pos), _ptr(q_rot),
+                                    _ptr(k_rot), _ptr(out), _ptr(lse), B, N, Hq, Hkv, D, code, sc,
+                                    float(base), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream))
+    _check("ks_evict_attn_fwd_rope", st)
+    return out, lse, q_rot, k_rot
+
+
+def ks_evict_attn_bwd_rope(q_rot, k_rot, v, e, pos, o, lse, dout, base=10000.0, scale=None,
+                           dq=None, dk=None, dv=None, ws=None, stream=None):
+    """Gradients of ks_evict_attn_fwd_rope with respect to the unrotated q and
+    k (and v).  Returns (dq, dk, dv)."""
+    lib = load_library()
+    B, N, Hq, D = q_rot.shape
+    Hkv = k_rot.shape[2]
+    for name, t in (("q_rot", q_rot), ("k_rot", k_rot), ("v", v), ("o", o), ("dout", dout)):
+        _cuda_contig(name, t, q_rot.dtype)
+    _cuda_contig("e", e, torch.int32)
+    _cuda_contig("pos", pos, torch.int32)
+    _cuda_contig("lse", lse, torch.float32)
+    _need(tuple(k_rot.shape) == (B, N, Hkv, D) and tuple(v.shape) == (B, N, Hkv, D),
+          "k/v shape")
+    _need(tuple(e.shape) == (B, N) and tuple(pos.shape) == (B, N), "e/pos must be [B, N]")
+    _need(tuple(o.shape) == tuple(q_rot.shape) and tuple(dout.shape) == tuple(q_rot.shape),
+          "o/dout")
+    _need(tuple(lse.shape) == (B, Hq, N), "lse must be [B, Hq, N]")
+    dq = torch.empty_like(q_rot) if dq is None else _given("dq", dq, q_rot.shape, q_rot.dtype)
+    dk = torch.empty_like(k_rot) if dk is None else _given("dk", dk, k_rot.shape, q_rot.dtype)
+    dv = torch.empty_like(v) if dv is None else _given("dv", dv, v.shape, q_rot.dtype)
+    code = _dtype_code(q_rot)
+    nbytes = lib.ks_evict_attn_bwd_rope_workspace(B, N, Hq, Hkv, D, code)
+    ws = _workspace(nbytes, q_rot.device, ws)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.ks_evict_attn_bwd_rope(_ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(e), _ptr(pos),
+                                    _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    B, N, Hq, Hkv, D, code, sc, float(base), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream))
+    _check("ks_evict_attn_bwd_rope", st)
     return dq, dk, dv
 
 

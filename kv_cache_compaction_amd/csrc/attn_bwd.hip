@@ -71,12 +71,35 @@ __device__ __forceinline__ int chunk_slot_rc(int s) {
   return tile_prow(p) | (min(c, 15) << 5);
 }
 
+// Gradients of the RoPE-fused path are with respect to the unrotated q and
+// k: the fp32 gradient row (blocks acc[db], rows d = 32 db + 8 rg + 4 lh + c)
+// is rotated by -theta before it is stored.  tr: the row's (cos, sin) pairs.
+__device__ __forceinline__ void rotate_back(f32x16 (&acc)[NDB], const float2* tr, int lh) {
+#pragma unroll
+  for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4* p4 = reinterpret_cast<const f32x4*>(tr + 32 * db + 8 * rg + 4 * lh);
+      const f32x4 a = p4[0], c = p4[1];
+      const float2 cs[4] = {make_float2(a[0], -a[1]), make_float2(a[2], -a[3]),
+                            make_float2(c[0], -c[1]), make_float2(c[2], -c[3])};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = acc[db][rg * 4 + i], y = acc[db + 2][rg * 4 + i];
+        rope_rotate(x, y, cs[i]);
+        acc[db][rg * 4 + i] = x;
+        acc[db + 2][rg * 4 + i] = y;
+      }
+    }
+}
+
+template <bool ROPE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ e, const int32_t* __restrict__ emin,
     const int32_t* __restrict__ emax, const float* __restrict__ rec,
     const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int B,
-    int N, int Npad, int Hq, int Hkv, int ntiles, float scale) {
+    int N, int Npad, int Hq, int Hkv, int ntiles, float scale, const float2* __restrict__ rtab) {
   __shared__ __attribute__((aligned(16))) bf16_t Vst[KW * kTileRow];
   __shared__ __attribute__((aligned(16))) bf16_t C0[CELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t C1[CELEMS];
@@ -300,6 +323,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // lane holds key jl; rows of dK^T / dV^T are d = 32 db + 8 rg + 4 lh + c
   if (jl < N) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dka[db][r] *= scale;
+    if constexpr (ROPE) {
+      // gradient with respect to the unrotated key: rotate back by -theta
+      // (pairs (d, d + 64) are blocks db and db + 2 of this lane)
+      rotate_back(dka, rtab + (static_cast<size_t>(b) * N + jl) * (D / 2), lh);
+    }
     const size_t off = (static_cast<size_t>(b) * N + jl) * tokkv + static_cast<size_t>(hkv) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -307,8 +339,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int rg = 0; rg < 4; ++rg) {
         const int d = db * 32 + rg * 8 + lh * 4;
         *reinterpret_cast<u32x2*>(dk + off + d) =
-            u32x2{pack_bf16x2(dka[db][rg * 4] * scale, dka[db][rg * 4 + 1] * scale),
-                  pack_bf16x2(dka[db][rg * 4 + 2] * scale, dka[db][rg * 4 + 3] * scale)};
+            u32x2{pack_bf16x2(dka[db][rg * 4], dka[db][rg * 4 + 1]),
+                  pack_bf16x2(dka[db][rg * 4 + 2], dka[db][rg * 4 + 3])};
         *reinterpret_cast<u32x2*>(dv + off + d) =
             u32x2{pack_bf16x2(dva[db][rg * 4], dva[db][rg * 4 + 1]),
                   pack_bf16x2(dva[db][rg * 4 + 2], dva[db][rg * 4 + 3])};
@@ -320,12 +352,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // dQ: laid out like the forward, 32 query rows per wave; key tiles of K and
 // V staged natural, K^T operands by transpose reads.
 // ---------------------------------------------------------------------------
-template <int HPW>
+template <int HPW, bool ROPE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const TileSummary ts, float* __restrict__ rec, const bf16_t* __restrict__ o,
     const float* __restrict__ lse, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
-    int B, int N, int Npad, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale) {
+    int B, int N, int Npad, int Hq, int Hkv, int ntiles, int nqt, int total_wg, float scale,
+    const float2* __restrict__ rtab) {
   constexpr int RS = 8 / HPW;
   constexpr int BM = 32 * RS;
   __shared__ __attribute__((aligned(16))) bf16_t S0[kKvElems];
@@ -495,6 +528,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   if (qi < N) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqa[db][r] *= scale;
+    if constexpr (ROPE)  // gradient with respect to the unrotated query
+      rotate_back(dqa, rtab + (static_cast<size_t>(b) * N + qi) * (D / 2), lh);
     bf16_t* op = dq + (static_cast<size_t>(b) * N + qi) * tokq + static_cast<size_t>(hq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -502,9 +541,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int rg = 0; rg < 4; ++rg) {
         const int d = db * 32 + rg * 8 + lh * 4;
         const f32x16& a = dqa[db];
-        *reinterpret_cast<u32x2*>(op + d) =
-            u32x2{pack_bf16x2(a[rg * 4] * scale, a[rg * 4 + 1] * scale),
-                  pack_bf16x2(a[rg * 4 + 2] * scale, a[rg * 4 + 3] * scale)};
+        *reinterpret_cast<u32x2*>(op + d) = u32x2{pack_bf16x2(a[rg * 4], a[rg * 4 + 1]),
+                                                  pack_bf16x2(a[rg * 4 + 2], a[rg * 4 + 3])};
       }
   }
 }
@@ -530,6 +568,60 @@ extern "C" size_t ks_evict_attn_bwd_workspace(int B, int N, int Hq, int Hkv, int
   return summary_bytes(B, N) + 2 * di_bytes(B, N, Hq);
 }
 
+namespace {
+
+// The two backward launches (dQ, then dK/dV) after the argument checks;
+// rtab non-null selects the kernels that rotate the gradients back.
+ks_status launch_bwd(const char* name, const bf16_t* qq, const bf16_t* kk, const bf16_t* vv,
+                     const int32_t* e, const bf16_t* oo, const float* lse, const bf16_t* gg,
+                     bf16_t* dq, bf16_t* dk, bf16_t* dv, int B, int N, int Hq, int Hkv,
+                     float scale, void* ws, const float2* rtab, hipStream_t s) {
+  const int hpw = ks_heads_per_wave(Hq / Hkv);
+  TileSummary ts;
+  ks_status st = launch_summary(e, ws, B, N, s, &ts);
+  if (st != KS_OK) return st;
+  float* rec = reinterpret_cast<float*>(static_cast<char*>(ws) + summary_bytes(B, N));
+  const int Npad = padded_rows(N);
+  const int ntiles = (N + kKeyTile - 1) / kKeyTile;
+
+  // dQ first: it forms D_i and the LSE records of every row, which dK/dV reads
+  const int rs = 8 / hpw;
+  const int nqt = (N + 32 * rs - 1) / (32 * rs);
+  const long long real_q = static_cast<long long>(B) * (Hq / hpw) * nqt;
+  const long long total_q = (real_q + 7) / 8 * 8;
+  KS_REQUIRE(total_q < (1LL << 31), "%s: grid too large", name);
+  const int nkt = (N + KW - 1) / KW;
+  const long long nkv = static_cast<long long>(B) * Hkv * nkt;
+  KS_REQUIRE(nkv < (1LL << 31), "%s: grid too large", name);
+#define KS_DQ_LAUNCH(HPW_, R_)                                                                 \
+  hipLaunchKernelGGL((dq_kernel<HPW_, R_>), dim3(static_cast<unsigned>(total_q)), dim3(512), 0, \
+                     s, qq, kk, vv, ts, rec, oo, lse, gg, dq, B, N, Npad, Hq, Hkv, ntiles, nqt, \
+                     static_cast<int>(total_q), scale, rtab)
+  if (rtab) {
+    if (hpw == 4) KS_DQ_LAUNCH(4, true);
+    else if (hpw == 2) KS_DQ_LAUNCH(2, true);
+    else KS_DQ_LAUNCH(1, true);
+  } else {
+    if (hpw == 4) KS_DQ_LAUNCH(4, false);
+    else if (hpw == 2) KS_DQ_LAUNCH(2, false);
+    else KS_DQ_LAUNCH(1, false);
+  }
+#undef KS_DQ_LAUNCH
+  st = ks_check_launch(name);
+  if (st != KS_OK) return st;
+  if (rtab)
+    hipLaunchKernelGGL(dkdv_kernel<true>, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq,
+                       kk, vv, e, ts.emin, ts.emax, rec, gg, dk, dv, B, N, Npad, Hq, Hkv, ntiles,
+                       scale, rtab);
+  else
+    hipLaunchKernelGGL(dkdv_kernel<false>, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq,
+                       kk, vv, e, ts.emin, ts.emax, rec, gg, dk, dv, B, N, Npad, Hq, Hkv, ntiles,
+                       scale, rtab);
+  return ks_check_launch(name);
+}
+
+}  // namespace
+
 extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void* v,
                                        const int32_t* e, const void* o, const float* lse,
                                        const void* dout, void* dq, void* dk, void* dv, int B,
@@ -541,8 +633,6 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
   if (dtype != KS_BF16 || Dh != D)
     return ks_fail(KS_ERR_UNSUPPORTED, "ks_evict_attn_bwd: only bf16 with D=128 (dtype=%d D=%d)",
                    dtype, Dh);
-  const int G = Hq / Hkv;
-  const int hpw = ks_heads_per_wave(G);
   if (B == 0 || N == 0) return KS_OK;
   KS_REQUIRE(q && k && v && e && o && lse && dout && dq && dk && dv,
              "ks_evict_attn_bwd: null pointer");
@@ -554,43 +644,62 @@ extern "C" ks_status ks_evict_attn_bwd(const void* q, const void* k, const void*
     return ks_fail(KS_ERR_WORKSPACE, "ks_evict_attn_bwd: workspace %zu < %zu bytes", ws_bytes,
                    need);
   KS_REQUIRE(ks_aligned16(ws), "ks_evict_attn_bwd: workspace must be 16-byte aligned");
+  return launch_bwd("ks_evict_attn_bwd", static_cast<const bf16_t*>(q),
+                    static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), e,
+                    static_cast<const bf16_t*>(o), lse, static_cast<const bf16_t*>(dout),
+                    static_cast<bf16_t*>(dq), static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv),
+                    B, N, Hq, Hkv, scale, ws, nullptr, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the RoPE-fused forward.  The forward's rotated q and k (q_rot,
+// k_rot) are the operands; the (cos, sin) table of the logical positions is
+// formed again in the workspace, and dQ and dK are rotated back by -theta in
+// fp32 before their bf16 store, so they are the gradients with respect to
+// the unrotated projections (the rotation is orthogonal, its transpose is
+// its inverse; explainer, RoPE paragraph, for the logical positions).
+// ---------------------------------------------------------------------------
+extern "C" size_t ks_evict_attn_bwd_rope_workspace(int B, int N, int Hq, int Hkv, int Dh,
+                                                   int dtype) {
+  (void)Hkv;
+  (void)dtype;
+  if (B <= 0 || N <= 0 || Hq <= 0 || Dh <= 0) return 0;
+  return summary_bytes(B, N) + 2 * di_bytes(B, N, Hq) + rope_table_bytes(B, N, Dh);
+}
+
+extern "C" ks_status ks_evict_attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v,
+                                            const int32_t* e, const int32_t* pos, const void* o,
+                                            const float* lse, const void* dout, void* dq,
+                                            void* dk, void* dv, int B, int N, int Hq, int Hkv,
+                                            int Dh, int dtype, float scale, float base, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  const char* name = "ks_evict_attn_bwd_rope";
+  KS_REQUIRE(B >= 0 && N >= 0 && Hq > 0 && Hkv > 0, "%s: bad sizes", name);
+  KS_REQUIRE(Hq % Hkv == 0, "%s: Hq %% Hkv != 0", name);
+  KS_REQUIRE(scale > 0.f, "%s: scale must be positive", name);
+  KS_REQUIRE(base > 1.0f, "%s: base must be > 1", name);
+  if (dtype != KS_BF16 || Dh != D)
+    return ks_fail(KS_ERR_UNSUPPORTED, "%s: only bf16 with D=128 (dtype=%d D=%d)", name, dtype,
+                   Dh);
+  if (B == 0 || N == 0) return KS_OK;
+  KS_REQUIRE(q_rot && k_rot && v && e && pos && o && lse && dout && dq && dk && dv,
+             "%s: null pointer", name);
+  KS_REQUIRE(ks_aligned16(q_rot) && ks_aligned16(k_rot) && ks_aligned16(v) && ks_aligned16(o) &&
+                 ks_aligned16(dout) && ks_aligned16(dq) && ks_aligned16(dk) && ks_aligned16(dv),
+             "%s: tensors must be 16-byte aligned", name);
+  const size_t base_need = summary_bytes(B, N) + 2 * di_bytes(B, N, Hq);
+  const size_t need = base_need + rope_table_bytes(B, N, Dh);
+  if (!ws || ws_bytes < need)
+    return ks_fail(KS_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
+  KS_REQUIRE(ks_aligned16(ws), "%s: workspace must be 16-byte aligned", name);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  TileSummary ts;
-  ks_status st = launch_summary(e, ws, B, N, s, &ts);
+  float2* table = reinterpret_cast<float2*>(static_cast<char*>(ws) + base_need);
+  ks_status st = launch_rope_prep(nullptr, nullptr, pos, table, static_cast<long long>(B) * N,
+                                  Hkv, Dh, base, s);
   if (st != KS_OK) return st;
-  const int32_t* emin = ts.emin;
-  const int32_t* emax = ts.emax;
-  float* rec = reinterpret_cast<float*>(static_cast<char*>(ws) + summary_bytes(B, N));
-  const int Npad = padded_rows(N);
-  const int ntiles = (N + kKeyTile - 1) / kKeyTile;
-  const bf16_t* qq = static_cast<const bf16_t*>(q);
-  const bf16_t* kk = static_cast<const bf16_t*>(k);
-  const bf16_t* vv = static_cast<const bf16_t*>(v);
-  const bf16_t* gg = static_cast<const bf16_t*>(dout);
-
-  // dQ first: it forms D_i and the LSE records of every row, which dK/dV reads
-  const int rs = 8 / hpw;
-  const int nqt = (N + 32 * rs - 1) / (32 * rs);
-  const long long real_q = static_cast<long long>(B) * (Hq / hpw) * nqt;
-  const long long total_q = (real_q + 7) / 8 * 8;
-  KS_REQUIRE(total_q < (1LL << 31), "ks_evict_attn_bwd: grid too large");
-  const int nkt = (N + KW - 1) / KW;
-  const long long nkv = static_cast<long long>(B) * Hkv * nkt;
-  KS_REQUIRE(nkv < (1LL << 31), "ks_evict_attn_bwd: grid too large");
-  const bf16_t* oo = static_cast<const bf16_t*>(o);
-#define KS_DQ_LAUNCH(HPW_)                                                                   \
-  hipLaunchKernelGGL((dq_kernel<HPW_>), dim3(static_cast<unsigned>(total_q)), dim3(512), \
-                     0, s, qq, kk, vv, ts, rec, oo, lse, gg, static_cast<bf16_t*>(dq), B, N, \
-                     Npad, Hq, Hkv, ntiles, nqt, static_cast<int>(total_q), scale)
-  if (hpw == 4) KS_DQ_LAUNCH(4);
-  else if (hpw == 2) KS_DQ_LAUNCH(2);
-  else KS_DQ_LAUNCH(1);
-#undef KS_DQ_LAUNCH
-  st = ks_check_launch("ks_evict_attn_bwd(dq)");
-  if (st != KS_OK) return st;
-
-  hipLaunchKernelGGL(dkdv_kernel, dim3(static_cast<unsigned>(nkv)), dim3(512), 0, s, qq, kk,
-                     vv, e, emin, emax, rec, gg, static_cast<bf16_t*>(dk),
-                     static_cast<bf16_t*>(dv), B, N, Npad, Hq, Hkv, ntiles, scale);
-  return ks_check_launch("ks_evict_attn_bwd(dkdv)");
+  return launch_bwd(name, static_cast<const bf16_t*>(q_rot), static_cast<const bf16_t*>(k_rot),
+                    static_cast<const bf16_t*>(v), e, static_cast<const bf16_t*>(o), lse,
+                    static_cast<const bf16_t*>(dout), static_cast<bf16_t*>(dq),
+                    static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), B, N, Hq, Hkv, scale, ws,
+                    table, s);
 }

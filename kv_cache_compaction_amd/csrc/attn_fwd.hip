@@ -432,11 +432,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Per key tile and wave: S^T = K Q^T (16 MFMAs), masked lazily-rescaled
 // softmax on 32 scores per lane, O^T += V^T P^T (16 MFMAs).
 // ---------------------------------------------------------------------------
-template <int HPW>
+template <int HPW, bool ROPE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_d128_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const TileSummary ts, bf16_t* __restrict__ o, float* __restrict__ lse, int B, int N, int Hq,
-    int Hkv, int ntiles, int nqt, int total_wg, float sl2) {
+    int Hkv, int ntiles, int nqt, int total_wg, float sl2, const float2* __restrict__ rtab,
+    bf16_t* __restrict__ q_rot) {
   constexpr int D = 128;
   constexpr int RS = 8 / HPW;   // 32-row subtiles per workgroup
   constexpr int BM = 32 * RS;   // query rows per workgroup
@@ -488,6 +489,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       u32x4 x = *reinterpret_cast<const u32x4*>(qp + s * 16);
       if (qi >= N) x = u32x4{0u, 0u, 0u, 0u};
       qf[s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  if constexpr (ROPE) {
+    // q arrives unrotated: rotate the row at its logical position (pairs
+    // (d, d + 64) are fragments s and s + 4 of this lane) with the prepared
+    // (cos, sin) pairs, and write the rotated row for the backward
+    if (qi < N) {
+      const float2* tr = rtab + (static_cast<size_t>(b) * N + qi) * (D / 2) + lh * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float2 cs[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 x = reinterpret_cast<const f32x4*>(tr + 16 * s)[u];
+          cs[2 * u] = make_float2(x[0], x[1]);
+          cs[2 * u + 1] = make_float2(x[2], x[3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float x = static_cast<float>(qf[s][i]), y = static_cast<float>(qf[s + 4][i]);
+          rope_rotate(x, y, cs[i]);
+          qf[s][i] = static_cast<__bf16>(x);
+          qf[s + 4][i] = static_cast<__bf16>(y);
+        }
+      }
+      bf16_t* qo = q_rot + (static_cast<size_t>(b) * N + qi) * Hq * D +
+                   static_cast<size_t>(hq) * D + lh * 8;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        *reinterpret_cast<u32x4*>(qo + s * 16) = __builtin_bit_cast(u32x4, qf[s]);
     }
   }
   wait_vm<0>();  // Q is in registers before the DMA stream starts
@@ -712,9 +743,9 @@ extern "C" ks_status ks_evict_attn_fwd(const void* q, const void* k, const void*
     const long long total8 = (real8 + 7) / 8 * 8;
     KS_REQUIRE(total8 < (1LL << 31), "ks_evict_attn_fwd: grid too large");
 #define KS_FWD128_LAUNCH(HPW_)                                                                 \
-  hipLaunchKernelGGL((fwd_d128_kernel<HPW_>), dim3(static_cast<unsigned>(total8)), dim3(512), 0, \
-                     s, qq, kk, vv, ts, oo, lse, B, N, Hq, Hkv, ntiles, nqt8,                     \
-                     static_cast<int>(total8), sl2)
+  hipLaunchKernelGGL((fwd_d128_kernel<HPW_, false>), dim3(static_cast<unsigned>(total8)),       \
+                     dim3(512), 0, s, qq, kk, vv, ts, oo, lse, B, N, Hq, Hkv, ntiles, nqt8,       \
+                     static_cast<int>(total8), sl2, nullptr, nullptr)
     if (hpw == 4) KS_FWD128_LAUNCH(4);
     else if (hpw == 2) KS_FWD128_LAUNCH(2);
     else KS_FWD128_LAUNCH(1);
@@ -726,4 +757,86 @@ extern "C" ks_status ks_evict_attn_fwd(const void* q, const void* k, const void*
   }
 #undef KS_FWD_LAUNCH
   return ks_check_launch("ks_evict_attn_fwd(bf16)");
+}
+
+// ---------------------------------------------------------------------------
+// RoPE fused into the forward: q and k arrive unrotated.  The preparation
+// kernel writes the (cos, sin) table of every token's logical position and
+// the rotated keys (k_rot), next to the per-tile e summary; the forward
+// kernel rotates each query row in registers as it loads it and writes the
+// rotated row (q_rot) for the backward.  New queries and keys continue the
+// original position count (explainer, RoPE paragraph), so the caller passes
+// logical positions.
+// ---------------------------------------------------------------------------
+extern "C" size_t ks_evict_attn_fwd_rope_workspace(int B, int N, int Hq, int Hkv, int D,
+                                                   int dtype) {
+  (void)Hq;
+  (void)Hkv;
+  (void)dtype;
+  if (B <= 0 || N <= 0 || D <= 0) return 0;
+  return summary_bytes(B, N) + rope_table_bytes(B, N, D);
+}
+
+extern "C" ks_status ks_evict_attn_fwd_rope(const void* q, const void* k, const void* v,
+                                            const int32_t* e, const int32_t* pos, void* q_rot,
+                                            void* k_rot, void* o, float* lse, int B, int N,
+                                            int Hq, int Hkv, int D, int dtype, float scale,
+                                            float base, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  const char* name = "ks_evict_attn_fwd_rope";
+  KS_REQUIRE(B >= 0 && N >= 0 && Hq > 0 && Hkv > 0, "%s: bad sizes", name);
+  KS_REQUIRE(Hq % Hkv == 0, "%s: Hq %% Hkv != 0", name);
+  KS_REQUIRE(scale > 0.f, "%s: scale must be positive", name);
+  KS_REQUIRE(base > 1.0f, "%s: base must be > 1", name);
+  if (dtype != KS_BF16 || D != 128)
+    return ks_fail(KS_ERR_UNSUPPORTED, "%s: only bf16 with D=128 (dtype=%d D=%d)", name, dtype,
+                   D);
+  const int hpw = ks_heads_per_wave(Hq / Hkv);
+  if (B == 0 || N == 0) return KS_OK;
+  KS_REQUIRE(q && k && v && e && pos && q_rot && k_rot && o && lse, "%s: null pointer", name);
+  KS_REQUIRE(ks_aligned16(q) && ks_aligned16(k) && ks_aligned16(v) && ks_aligned16(o) &&
+                 ks_aligned16(q_rot) && ks_aligned16(k_rot),
+             "%s: tensors must be 16-byte aligned", name);
+  const size_t nq = static_cast<size_t>(B) * N * Hq * D * 2, nk = static_cast<size_t>(B) * N *
+                                                                   Hkv * D * 2;
+  auto overlap = [](const void* a, size_t na, const void* c, size_t nc) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(c);
+    return x < y + nc && y < x + na;
+  };
+  KS_REQUIRE(!overlap(q, nq, q_rot, nq) && !overlap(k, nk, k_rot, nk),
+             "%s: q_rot and k_rot must not alias q and k", name);
+  const size_t need = summary_bytes(B, N) + rope_table_bytes(B, N, D);
+  if (!ws || ws_bytes < need)
+    return ks_fail(KS_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
+  KS_REQUIRE(ks_aligned16(ws), "%s: workspace must be 16-byte aligned", name);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* table = reinterpret_cast<float2*>(static_cast<char*>(ws) + summary_bytes(B, N));
+  ks_status st = launch_rope_prep(static_cast<const bf16_t*>(k), static_cast<bf16_t*>(k_rot), pos,
+                                  table, static_cast<long long>(B) * N, Hkv, D, base, s);
+  if (st != KS_OK) return st;
+  TileSummary ts;
+  st = launch_summary(e, ws, B, N, s, &ts);
+  if (st != KS_OK) return st;
+  const int ntiles = (N + kKeyTile - 1) / kKeyTile;
+  const float sl2 = scale * KS_LOG2E;
+  const int rs8 = 8 / hpw;
+  const int nqt8 = (N + 32 * rs8 - 1) / (32 * rs8);
+  const long long real8 = static_cast<long long>(B) * (Hq / hpw) * nqt8;
+  const long long total8 = (real8 + 7) / 8 * 8;
+  KS_REQUIRE(total8 < (1LL << 31), "%s: grid too large", name);
+  const bf16_t* qq = static_cast<const bf16_t*>(q);
+  const bf16_t* kk = static_cast<const bf16_t*>(k_rot);
+  const bf16_t* vv = static_cast<const bf16_t*>(v);
+  bf16_t* oo = static_cast<bf16_t*>(o);
+  bf16_t* qr = static_cast<bf16_t*>(q_rot);
+#define KS_FWD128_ROPE(HPW_)                                                                  \
+  hipLaunchKernelGGL((fwd_d128_kernel<HPW_, true>), dim3(static_cast<unsigned>(total8)),      \
+                     dim3(512), 0, s, qq, kk, vv, ts, oo, lse, B, N, Hq, Hkv, ntiles, nqt8,     \
+                     static_cast<int>(total8), sl2, table, qr)
+  if (hpw == 4) KS_FWD128_ROPE(4);
+  else if (hpw == 2) KS_FWD128_ROPE(2);
+  else KS_FWD128_ROPE(1);
+#undef KS_FWD128_ROPE
+  return ks_check_launch(name);
 }

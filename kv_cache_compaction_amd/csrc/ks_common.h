@@ -21,6 +21,14 @@ typedef uint16_t bf16_t;  // storage type of one bf16 value
 ks_status ks_fail(ks_status st, const char* fmt, ...);
 ks_status ks_check_launch(const char* what);
 
+// RoPE preparation of the fused attention entry points (rope.hip): the
+// (cos, sin) table of every token's logical position ([B*N][D/2] float2)
+// and, when k_raw is non-null, the keys rotated out of place into k_rot
+size_t rope_table_bytes(int B, int N, int D);
+ks_status launch_rope_prep(const uint16_t* k_raw, uint16_t* k_rot, const int32_t* pos,
+                           float2* table, long long ntok, int Hkv, int D, float base,
+                           hipStream_t s);
+
 #define KS_REQUIRE(cond, ...)                                  \
   do {                                                         \
     if (!(cond)) return ks_fail(KS_ERR_INVALID_ARG, __VA_ARGS__); \

@@ -92,7 +92,63 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ q, T* __
   }
 }
 
+// Preparation of the RoPE-fused attention (bf16): per token, the (cos, sin)
+// pairs of its logical position go to `table` ([ntok][D/2] float2) and, when
+// k_raw is given, every kv head of its key is rotated out of place into k_rot.
+// The pairs are rope_cos_sin's, so a row rotated with them is bit-identical
+// to ks_rope_logical's.
+__global__ __launch_bounds__(kThreads) void rope_prep_kernel(
+    const bf16_t* __restrict__ k_raw, bf16_t* __restrict__ k_rot, const int32_t* __restrict__ pos,
+    float2* __restrict__ table, long long ntok, int Hkv, int D, double log2_base) {
+  typedef u32x4 VT;
+  constexpr int V = 8;
+  __shared__ float2 cs[kTok][kMaxHalf];
+  const int half = D >> 1;
+  const long long t0 = static_cast<long long>(blockIdx.x) * kTok;
+  for (int idx = threadIdx.x; idx < kTok * half; idx += kThreads) {
+    const int tt = idx / half, kk = idx - tt * half;
+    const long long t = t0 + tt;
+    if (t < ntok) {
+      const float2 c = rope_cos_sin(static_cast<double>(pos[t]), kk, D, log2_base);
+      cs[tt][kk] = c;
+      table[t * half + kk] = c;
+    }
+  }
+  if (!k_raw) return;
+  __syncthreads();
+  const int cpr = half / V;  // chunks per head
+  const int per_tok = Hkv * cpr;
+  for (int idx = threadIdx.x; idx < kTok * per_tok; idx += kThreads) {
+    const int tt = idx / per_tok;
+    const int r = idx - tt * per_tok;
+    const long long t = t0 + tt;
+    if (t >= ntok) continue;
+    const int hh = r / cpr, ch = r - hh * cpr;
+    const long long off = (t * Hkv + hh) * static_cast<long long>(D) + ch * V;
+    VT a = *reinterpret_cast<const VT*>(k_raw + off);
+    VT b = *reinterpret_cast<const VT*>(k_raw + off + half);
+    rot_chunk(a, b, &cs[tt][ch * V]);
+    *reinterpret_cast<VT*>(k_rot + off) = a;
+    *reinterpret_cast<VT*>(k_rot + off + half) = b;
+  }
+}
+
 }  // namespace
+
+size_t rope_table_bytes(int B, int N, int D) {
+  return (static_cast<size_t>(B) * N * (D / 2) * sizeof(float2) + 255) &
+         ~static_cast<size_t>(255);
+}
+
+ks_status launch_rope_prep(const bf16_t* k_raw, bf16_t* k_rot, const int32_t* pos,
+                           float2* table, long long ntok, int Hkv, int D, float base,
+                           hipStream_t s) {
+  const long long nblocks = (ntok + kTok - 1) / kTok;
+  if (nblocks >= (1LL << 31)) return ks_fail(KS_ERR_INVALID_ARG, "RoPE preparation: too many tokens");
+  hipLaunchKernelGGL(rope_prep_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s,
+                     k_raw, k_rot, pos, table, ntok, Hkv, D, log2(static_cast<double>(base)));
+  return ks_check_launch("RoPE preparation");
+}
 
 extern "C" ks_status ks_rope_logical(void* q, void* k, const int32_t* pos, int B, int N, int Hq,
                                      int Hkv, int D, int dtype, float base, int inverse,

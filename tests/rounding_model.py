@@ -24,10 +24,13 @@ def bf16_round(x):
     return t.to(torch.bfloat16).to(torch.float64).numpy()
 
 
-def dq_rows(q, k, v, e, do, b, h, rows, scale=None, rounding=True):
+def dq_rows(q, k, v, e, do, b, h, rows, scale=None, rounding=True, pos=None):
     """dQ of rows ``rows`` of query head ``h`` of trace ``b`` as the kernels
     round it.  q, k: rotated (fp64 or bf16 values); v, do: bf16 values.
-    ``rounding=False`` skips every rounding point (plain fp64 dQ)."""
+    ``rounding=False`` skips every rounding point (plain fp64 dQ).  With
+    ``pos`` (the rows' logical positions) the gradient is rotated back by
+    -theta before its final rounding, as the RoPE-fused backward stores the
+    gradient of the unrotated query."""
     rnd = bf16_round if rounding else (lambda x: np.asarray(x, dtype=np.float64))
     Hq, Hkv, D = q.shape[2], k.shape[2], q.shape[3]
     kv = h // (Hq // Hkv)
@@ -54,4 +57,16 @@ def dq_rows(q, k, v, e, do, b, h, rows, scale=None, rounding=True):
     dP = dd @ vv.T
     Di = (dd * o).sum(axis=1, keepdims=True)
     dS = rnd(P * (dP - Di))
-    return rnd(sc * (dS @ kk))
+    g = sc * (dS @ kk)
+    if pos is not None:
+        g = unrotate_rows(g, pos)
+    return rnd(g)
+
+
+def unrotate_rows(x, pos, base=10000.0):
+    """Rotate rows x [n, D] by -theta at positions pos [n] (rotate-half
+    pairing, fp64): the backward of RoPE for gradient rows."""
+    import oracle as O
+
+    x = np.asarray(x, dtype=np.float64)
+    return O.rope(x[None, :, None, :], np.asarray(pos)[None], base, inverse=True)[0, :, 0]

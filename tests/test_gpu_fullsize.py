@@ -30,9 +30,12 @@ def _sample_rows(tr, rng, n=40):
     return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
-def check_rows(o, lse, dq, q_raw, k_raw, v_h, do_h, e, b, hkv, rows, tag=""):
+def check_rows(o, lse, dq, q_raw, k_raw, v_h, do_h, e, b, hkv, rows, tag="", unrotated=False):
     """Forward and dQ rows of one (trace, kv group) against the oracle; the
-    dQ gate is tied to the rounding model (parity_util.gate_rows_model)."""
+    dQ gate is tied to the rounding model (parity_util.gate_rows_model).
+    ``unrotated``: dq holds gradients of the unrotated queries (the RoPE-
+    fused backward), so the oracle's rows are rotated back at their
+    positions (0..N-1 here)."""
     N = q_raw.shape[1]
     G = q_raw.shape[2]
     qs = O.rope(q_raw, np.arange(N)[None])
@@ -44,13 +47,17 @@ def check_rows(o, lse, dq, q_raw, k_raw, v_h, do_h, e, b, hkv, rows, tag=""):
         gate(o[b, rows, h], ro, "bf16", f"O rows{tag} h{h}")
         gate(lse[b, h, rows], rl, "bf16", f"LSE rows{tag} h{h}")
         rdq = O.attn_bwd_rows(qs, kk, v_h, eb, do_h, 0, hh, rows)
-        mdq = RM.dq_rows(qs, kk, v_h, eb, do_h, 0, hh, rows)
+        if unrotated:
+            rdq = RM.unrotate_rows(rdq, rows)
+        mdq = RM.dq_rows(qs, kk, v_h, eb, do_h, 0, hh, rows, pos=rows if unrotated else None)
         gate_rows_model(dq[b, rows, h], rdq, mdq, f"dQ rows{tag} h{h}")
     return qs, kk
 
 
 def run_training_config(cfg, b, hkv, key_blocks):
-    """The bench's launch on the full configuration; rows of every (trace,
+    """The bench's launch on the full configuration (RoPE fused into the
+    forward and backward; q and k are the unrotated projections at
+    positions 0..N-1, and the gradients are theirs); rows of every (trace,
     kv group) unit and key blocks of unit (b, hkv) against the oracle."""
     traces, seeds = config_trace_batch(cfg)
     e = stacked_e(traces)
@@ -61,18 +68,18 @@ def run_training_config(cfg, b, hkv, key_blocks):
     k = normal_tensor((B, N, Hkv, D), seeds["k"], cfg.value_scale, bf, DEV)
     v = normal_tensor((B, N, Hkv, D), seeds["v"], cfg.value_scale, bf, DEV)
     do = normal_tensor((B, N, Hq, D), seeds["do"], cfg.value_scale, bf, DEV)
-    # raw (unrotated) projections stay on the host for the oracle
     q_raw, k_raw = q.cpu(), k.cpu()
     pos = torch.arange(N, dtype=torch.int32, device=DEV)[None].repeat(B, 1).contiguous()
-    ks.ks_rope_logical(q, k, pos)
     eg = torch.from_numpy(e).to(DEV)
-    o, lse = ks.ks_evict_attn_fwd(q, k, v, eg)
-    dq, dk, dv = ks.ks_evict_attn_bwd(q, k, v, eg, o, lse, do)
+    o, lse, q_rot, k_rot = ks.ks_evict_attn_fwd_rope(q, k, v, eg, pos)
+    dq, dk, dv = ks.ks_evict_attn_bwd_rope(q_rot, k_rot, v, eg, pos, o, lse, do)
+    del q_rot, k_rot
     torch.cuda.synchronize()
 
     # properties over every trace and head: softmax rows sum to one, so the
     # dV of a kv group sums to the dO of its query heads; S is bilinear in
-    # (q, k), so sum q.dq = sum k.dk
+    # (q, k), so sum q.dq = sum k.dk (also for the unrotated projections
+    # and their gradients: the rotation is orthogonal)
     sdv = dv.float().sum(1)                                   # [B, Hkv, D]
     sdo = do.float().sum(1).view(B, Hkv, G, D).sum(2)
     assert torch.allclose(sdv, sdo, atol=0.05 * sdo.abs().max().item()), \
@@ -97,13 +104,15 @@ def run_training_config(cfg, b, hkv, key_blocks):
                                 f64(k_raw[bb:bb + 1, :, gg:gg + 1]),
                                 f64(v_c[bb:bb + 1, :, gg:gg + 1]),
                                 f64(do_c[bb:bb + 1, :, heads]), e, bb, gg, rows,
-                                tag=f" t{bb}")
+                                tag=f" t{bb}", unrotated=True)
             if not main:
                 continue
             v_h = f64(v_c[bb:bb + 1, :, gg:gg + 1])
             do_h = f64(do_c[bb:bb + 1, :, heads])
             blocks = key_blocks(traces[bb])
-            rdk, rdv = oracle_bwd_keys(qs, kk, v_h, e[bb:bb + 1], do_h, np.concatenate(blocks))
+            allk = np.concatenate(blocks)
+            rdk, rdv = oracle_bwd_keys(qs, kk, v_h, e[bb:bb + 1], do_h, allk)
+            rdk = RM.unrotate_rows(rdk, allk)               # keys at positions 0..N-1
             at = 0
             for keys in blocks:
                 sl = slice(at, at + len(keys))
