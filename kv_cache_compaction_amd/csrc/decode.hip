@@ -271,13 +271,35 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   const int L = min(max(seq_lens[b], 0), cap);
   const int ns = (((L + 15) >> 4) + kSplit - 1) / kSplit;
   const size_t slot0 = (static_cast<size_t>(b) * Hq + h) * nsplit_max;
+  // splits in groups of 8 whose loads are all issued before their use (a
+  // plain loop waits for each load in turn); the sums run in split order
+  constexpr int U = 8;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(slot0 + s) * 2]);
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float m[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) m[u] = s0 + u < ns ? part_ml[(slot0 + s0 + u) * 2] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, m[u]);
+  }
   float den = 0.f, num = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float f = fast_exp2(part_ml[(slot0 + s) * 2] - M);
-    den += part_ml[(slot0 + s) * 2 + 1] * f;
-    num += part_o[(slot0 + s) * D + d] * f;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float m[U], l[U], x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t sl = slot0 + min(s0 + u, ns - 1);
+      m[u] = part_ml[sl * 2];
+      l[u] = part_ml[sl * 2 + 1];
+      x[u] = part_o[sl * D + d];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < ns) {
+        const float f = fast_exp2(m[u] - M);
+        den += l[u] * f;
+        num += x[u] * f;
+      }
+    }
   }
   const size_t o = (static_cast<size_t>(b) * Hq + h) * D + d;
   if (ns == 0) {
