@@ -158,6 +158,63 @@ def test_decode_bs1_ragged_lengths(Hq, Hkv, seed):
     gate(lse[1:], rl, "bf16", "decode bs1 lse")
 
 
+# 8 kv heads (the workload's) with 1, 2 or 4 query heads per kv head, with
+# and without the in-kernel rotation of the query: lengths of a few tokens,
+# around the 16-token groups and 768-token splits, and a length past the
+# table's capacity (clamped to the row)
+@pytest.mark.parametrize("Hq,seed", [(8, 11), (16, 12), (32, 13)])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_decode_bs1_eight_kv_heads(Hq, seed, rotate):
+    Hkv, D = 8, 128
+    lens = np.array([0, 1, 2, 3, 15, 16, 17, 255, 767, 768, 769, 1537, 2500], np.int32)
+    B = len(lens)
+    q, kp, vp, table = _direct_bs1(B, Hq, Hkv, lens, 500 + seed)
+    lg = lens.copy()
+    lg[-1] = table.shape[1] + 40                  # beyond the row: clamped to MT
+    pos = (np.arange(B, dtype=np.int32) * 977 + 13) if rotate else None
+    if rotate:
+        out, lse = ks.ks_paged_decode_rope(q, _gpu(pos), kp, vp, _gpu(table), _gpu(lg))
+    else:
+        out, lse = ks.ks_paged_decode_bs1(q, kp, vp, _gpu(table), _gpu(lg))
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    qh = f64(q[1:])
+    if rotate:
+        qh = O.rope(qh[:, None], pos[1:, None])[:, 0]
+    lens_ref = lens[1:].copy()
+    lens_ref[-1] = table.shape[1]
+    kh = kp.float().cpu().numpy()[:, :, None]
+    vh = vp.float().cpu().numpy()[:, :, None]
+    ro, rl = O.paged_decode(qh, kh, vh, table[1:], lens_ref)
+    gate(out[1:], ro, "bf16", f"decode bs1 out Hq={Hq} rotate={rotate}")
+    gate(lse[1:], rl, "bf16", f"decode bs1 lse Hq={Hq} rotate={rotate}")
+
+
+def test_decode_bs1_rope_matches_separate_rotation():
+    """The in-kernel rotation of the query gives the same bits as rotating it
+    first with ks_rope_logical."""
+    lens = np.array([300, 1, 700], np.int32)
+    q, kp, vp, table = _direct_bs1(3, 32, 8, lens, 600)
+    pos = torch.tensor([12345, 7, 99999], dtype=torch.int32, device=DEV)
+    o1, l1 = ks.ks_paged_decode_rope(q, pos, kp, vp, _gpu(table), _gpu(lens))
+    qr = q.clone()
+    ks.ks_rope_logical(qr[:, None], None, pos[:, None].contiguous())
+    o2, l2 = ks.ks_paged_decode_bs1(qr, kp, vp, _gpu(table), _gpu(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_bs1_invalid_slot_in_a_later_split():
+    lens = np.array([40, 40, 1600], np.int32)
+    q, kp, vp, table = _direct_bs1(3, 32, 8, lens, 700)
+    table[1, 33] = kp.shape[0] + 5          # out of range
+    table[2, 1500] = -3                     # in the second 768-token split
+    out, _ = ks.ks_paged_decode_bs1(q, kp, vp, _gpu(table), _gpu(lens))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[0].float()).all()
+    assert torch.isnan(out[1].float()).all() and torch.isnan(out[2].float()).all()
+
+
 def test_decode_bs1_invalid_slot_gives_nan_not_fault():
     lens = np.array([40, 40, 40], np.int32)
     q, kp, vp, table = _direct_bs1(3, 4, 1, lens, 200)
