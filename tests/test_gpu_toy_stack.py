@@ -1,15 +1,16 @@
 """The toy decoder stack on the GPU: a 3-layer random-weight model whose
 attention is the KV-streams path.  Its masked training pass and its
 token-by-token generation over compacted paged caches are compared with the
-oracle's stack and with each other, by the KL divergence of the next-token
-distributions (the trainer/generator mismatch measure the pages quote)."""
+oracle's stack (logits element by element, and the KL divergence of the
+next-token distributions, the trainer/generator mismatch measure the pages
+quote) and with each other."""
 import numpy as np
 import pytest
 import torch
 
 from kv_cache_compaction_amd.toy_stack import ToyStack
 from oracle import toy_stack as T
-from parity_util import announce
+from parity_util import announce, errors
 from workloads import ToyShape, build_trace, check_trace, toy_tokens, toy_weights
 
 pytestmark = pytest.mark.gpu
@@ -21,6 +22,19 @@ SHAPE = ToyShape(layers=3, vocab=512, d_model=512, Hq=4, Hkv=2, D=128, ffn=1024)
 # (1e-2)^2 / 2 = 5e-5 per token.  The bounds leave a factor of ~10.
 KL_MEAN = 5e-4
 KL_MAX = 5e-3
+# element by element: the same ~24 bf16 roundings (2^-9 relative each) put an
+# rms error of about 2^-9 sqrt(24) ~ 1e-2 of the logits' rms (~1) on each
+# logit; measured 4.7e-3 (relative L2) and 6e-3 (max over max |ref|)
+LOGIT_REL_L2 = 1e-2
+LOGIT_REL_MAX = 1.5e-2
+
+
+def check_logits(got, ref, what):
+    er = errors(got, ref, "bf16")
+    announce(f"{what} logits: rel_l2 {er['rel_l2']:.3g} rel_max {er['rel_max']:.3g} "
+             f"max_abs {er['max_abs']:.3g}")
+    assert er["finite"] and er["rel_l2"] <= LOGIT_REL_L2 and er["rel_max"] <= LOGIT_REL_MAX, \
+        (what, er)
 
 
 @pytest.fixture(autouse=True)
@@ -46,6 +60,7 @@ def test_training_pass_matches_generation(strategy, seed):
     ref = T.train_logits(w, tok, tr.e, SHAPE.Hq, SHAPE.Hkv, SHAPE.D)
     lt, ld = lt.cpu().numpy(), ld.cpu().numpy()
     for name, got in (("train", lt), ("decode", ld)):
+        check_logits(got, ref, f"{strategy} {name}")
         kl = T.kl_rows(ref, got)
         announce(f"{strategy} {name} vs oracle: KL mean {kl.mean():.3g} max {kl.max():.3g}")
         assert np.isfinite(got).all()
@@ -78,6 +93,8 @@ def test_single_token_blocks_generation_matches():
     torch.cuda.synchronize()
     ref = T.train_logits(w, tok, tr.e, SHAPE.Hq, SHAPE.Hkv, SHAPE.D)
     lt, ld = lt.cpu().numpy(), ld.cpu().numpy()
+    check_logits(lt, ref, "single-token train")
+    check_logits(ld, ref, "single-token decode")
     for name, a, b in (("train vs oracle", ref, lt), ("decode vs oracle", ref, ld),
                        ("train vs decode (mismatch)", lt, ld)):
         kl = T.kl_rows(a, b)
