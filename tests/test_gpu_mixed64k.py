@@ -1,7 +1,8 @@
 """GPU parity of the long mixed workload: 8 traces of 65,536 tokens with
 window / prompt+recent / summary compaction, 64 q / 8 kv heads; masked
-forward + backward, then 256 decode steps per trace with a forced compaction
-after the 128th new token.  Sampled outputs are checked against the oracle
+forward + backward with RoPE fused in (the bench's launch: q and k are the
+raw projections, dq and dk their gradients), then 256 decode steps per trace
+with a forced compaction after the 128th new token.  Sampled outputs are checked against the oracle
 (rows and key blocks of one kv group per trace); properties over all."""
 import numpy as np
 import pytest
@@ -47,13 +48,13 @@ def run():
                      do=f64(do[b:b + 1, :, g * G:(g + 1) * G]))
         raw.append(d)
     pos = torch.arange(N, dtype=torch.int32, device=DEV)[None].repeat(B, 1).contiguous()
-    ks.ks_rope_logical(q, k, pos)
     eg = torch.from_numpy(e).to(DEV)
-    o, lse = ks.ks_evict_attn_fwd(q, k, v, eg)
-    dq, dk, dv = ks.ks_evict_attn_bwd(q, k, v, eg, o, lse, do)
+    o, lse, q_rot, k_rot = ks.ks_evict_attn_fwd_rope(q, k, v, eg, pos)
+    dq, dk, dv = ks.ks_evict_attn_bwd_rope(q_rot, k_rot, v, eg, pos, o, lse, do)
+    del q_rot
     torch.cuda.synchronize()
-    return dict(traces=traces, e=e, q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv,
-                raw=raw)
+    return dict(traces=traces, e=e, q=q, k=k, k_rot=k_rot, v=v, do=do, o=o, lse=lse, dq=dq,
+                dk=dk, dv=dv, raw=raw)
 
 
 def test_mixed64k_properties(run):
@@ -93,11 +94,14 @@ def test_mixed64k_sampled_rows_and_keys(run, b):
         ro, rl = O.attn_fwd_rows(qs, kk, r["v"], eb, 0, hh, rows)
         gate(run["o"][b, rows, h], ro, "bf16", f"O rows t{b} h{h}")
         gate(run["lse"][b, h, rows], rl, "bf16", f"LSE rows t{b} h{h}")
-        rdq = O.attn_bwd_rows(qs, kk, r["v"], eb, r["do"], 0, hh, rows)
-        mdq = RM.dq_rows(qs, kk, r["v"], eb, r["do"], 0, hh, rows)
+        # gradients of the raw projections: the oracle's rows rotated back
+        rdq = RM.unrotate_rows(O.attn_bwd_rows(qs, kk, r["v"], eb, r["do"], 0, hh, rows), rows)
+        mdq = RM.dq_rows(qs, kk, r["v"], eb, r["do"], 0, hh, rows, pos=rows)
         gate_rows_model(run["dq"][b, rows, h], rdq, mdq, f"dQ rows t{b} h{h}")
     blocks = key_blocks(tr)
-    rdk, rdv = oracle_bwd_keys(qs, kk, r["v"], eb, r["do"], np.concatenate(blocks))
+    allk = np.concatenate(blocks)
+    rdk, rdv = oracle_bwd_keys(qs, kk, r["v"], eb, r["do"], allk)
+    rdk = RM.unrotate_rows(rdk, allk)
     at = 0
     for keys in blocks:
         sl = slice(at, at + len(keys))
@@ -164,7 +168,7 @@ def test_mixed64k_decode_with_forced_compaction(run):
         blk = torch.from_numpy(np.repeat(table0[b, :L0[b] // BLOCK], BLOCK).astype(np.int64)).to(DEV)
         slot = torch.arange(L0[b], device=DEV) % BLOCK
         tok = torch.from_numpy(live_tok[b].astype(np.int64)).to(DEV)
-        kp[blk, :, slot] = run["k"][b, tok]
+        kp[blk, :, slot] = run["k_rot"][b, tok]
         vp[blk, :, slot] = run["v"][b, tok]
     # --- the forced event after token EVENT_AFTER: evicted spans per trace
     t_ev = N + EVENT_AFTER
