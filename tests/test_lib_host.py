@@ -207,3 +207,54 @@ def test_decode_workspace_query_covers_empty_tables(lib):
         assert getattr(lib, fn)(4, 32, 128, 0) == one
         assert getattr(lib, fn)(4, 32, 128, -3) == one
         assert getattr(lib, fn)(0, 32, 128, 0) == 0
+
+
+def test_fused_rope_attention_argument_checks(lib):
+    """The RoPE-fused training entry points refuse bad arguments before any
+    launch: fp32, D other than 128, base <= 1, outputs aliasing the inputs
+    they are rotated from, short workspaces; empty sizes are no-ops."""
+    B, N, H, D = 1, 64, 2, 128
+    big = ctypes.c_void_p(1 << 30)      # distinct aligned addresses, never dereferenced
+    q, k, qr, kr = (ctypes.c_void_p((i + 1) << 24) for i in range(4))
+    need_f = lib.ks_evict_attn_fwd_rope_workspace(B, N, H, H, D, ks.KS_BF16)
+    need_b = lib.ks_evict_attn_bwd_rope_workspace(B, N, H, H, D, ks.KS_BF16)
+    assert need_f > lib.ks_evict_attn_fwd_workspace(B, N, H, H, D, ks.KS_BF16)
+    assert need_b > lib.ks_evict_attn_bwd_workspace(B, N, H, H, D, ks.KS_BF16)
+    fwd = lambda *a: _status(lib, "ks_evict_attn_fwd_rope", *a)
+    st, _ = fwd(q, k, FAKE, FAKE, FAKE, qr, kr, FAKE, FAKE, B, N, H, H, D, ks.KS_F32, 0.1,
+                10000.0, big, need_f, None)
+    assert st == 2                                          # fp32: unsupported
+    st, _ = fwd(q, k, FAKE, FAKE, FAKE, qr, kr, FAKE, FAKE, B, N, H, H, 64, ks.KS_BF16, 0.1,
+                10000.0, big, need_f, None)
+    assert st == 2                                          # D = 64: unsupported
+    st, msg = fwd(q, k, FAKE, FAKE, FAKE, qr, kr, FAKE, FAKE, B, N, H, H, D, ks.KS_BF16, 0.1,
+                  1.0, big, need_f, None)
+    assert st == 1 and "base" in msg
+    st, msg = fwd(q, k, FAKE, FAKE, FAKE, q, kr, FAKE, FAKE, B, N, H, H, D, ks.KS_BF16, 0.1,
+                  10000.0, big, need_f, None)
+    assert st == 1 and "alias" in msg                       # q_rot is q
+    st, msg = fwd(q, k, FAKE, FAKE, FAKE, qr, k, FAKE, FAKE, B, N, H, H, D, ks.KS_BF16, 0.1,
+                  10000.0, big, need_f, None)
+    assert st == 1 and "alias" in msg                       # k_rot is k
+    st, _ = fwd(q, k, FAKE, FAKE, FAKE, qr, kr, FAKE, FAKE, B, N, H, H, D, ks.KS_BF16, 0.1,
+                10000.0, big, need_f - 1, None)
+    assert st == 4                                          # workspace short of the table
+    st, msg = fwd(q, k, FAKE, FAKE, FAKE, qr, kr, FAKE, None, B, N, H, H, D, ks.KS_BF16, 0.1,
+                  10000.0, big, need_f, None)
+    assert st == 1 and "null" in msg                        # lse is required
+    st, _ = fwd(None, None, None, None, None, None, None, None, None, 0, N, H, H, D, ks.KS_BF16,
+                0.1, 10000.0, None, 0, None)
+    assert st == 0                                          # B == 0 is a no-op
+    bwd = lambda *a: _status(lib, "ks_evict_attn_bwd_rope", *a)
+    st, _ = bwd(qr, kr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, N, H, H, D,
+                ks.KS_BF16, 0.1, 10000.0, big, need_b - 1, None)
+    assert st == 4                                          # workspace short of the table
+    st, msg = bwd(qr, kr, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, N, H, H, D,
+                  ks.KS_BF16, 0.1, 10000.0, big, need_b, None)
+    assert st == 1 and "null" in msg                        # pos is required
+    st, msg = bwd(qr, kr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, N, 3, H, D,
+                  ks.KS_BF16, 0.1, 10000.0, big, need_b, None)
+    assert st == 1 and "Hq" in msg
+    st, _ = bwd(None, None, None, None, None, None, None, None, None, None, None, B, 0, H, H, D,
+                ks.KS_BF16, 0.1, 10000.0, None, 0, None)
+    assert st == 0                                          # N == 0 is a no-op
