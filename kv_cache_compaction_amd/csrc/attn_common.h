@@ -117,6 +117,20 @@ __device__ __forceinline__ bf16x8 tile_frag_t(const bf16_t* t, int lane_t, int r
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// max and sum of x over the lane pair (l, l ^ 32): v_permlane32_swap
+// exchanges the two halves of the wave in registers (a VALU op; a shuffle
+// would go through LDS)
+__device__ __forceinline__ float max_lane_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_lane_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // acc + sum of the 8 bf16 values (packed dot products with (1, 1))
 __device__ __forceinline__ float sum_bf16x8(bf16x8 x, float acc) {
   const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};

@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         float mx = sv[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_lane_pair32(mx);
         const bool need = mx > mrow[qb] + kTau;
         if (__ballot(need)) {
           const float f = need ? fast_exp2(mrow[qb] - mx) : 1.f;
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // ---- epilogue ------------------------------------------------------------
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lt = lrow[qb] + __shfl_xor(lrow[qb], 32);
+    const float lt = sum_lane_pair32(lrow[qb]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a row that sees no key: O = 0
     const int i = wi0 + qb * 32 + lq;
     if (i < N) {
@@ -575,7 +575,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kk][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    mx = max_lane_pair32(mx) * sl2;
     const bool need = mx > mrow + kTau;
     if (__ballot(need)) {
       const float f = need ? fast_exp2(mrow - mx) : 1.f;
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     bar_nofence();
   }
 
-  const float ltot = lrow + __shfl_xor(lrow, 32);
+  const float ltot = sum_lane_pair32(lrow);
   if (qi < N) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // a row that sees no key: O = 0
     bf16_t* op = o + (static_cast<size_t>(b) * N + qi) * Hq * D + static_cast<size_t>(hq) * D;
