@@ -167,7 +167,8 @@ ks_status ks_evict_attn_bwd(const void* q, const void* k, const void* v,
  *
  * q      [B, N, Hq, D] unrotated queries;  k, v [B, N, Hkv, D]
  * e      int32 [B, N] as in ks_evict_attn_fwd; pos int32 [B, N] (device)
- * q_rot  [B, N, Hq, D], k_rot [B, N, Hkv, D] outputs; must not overlap q, k
+ * q_rot  [B, N, Hq, D], k_rot [B, N, Hkv, D] outputs; q_rot, k_rot and o
+ *        must not overlap q, k, v or each other (KS_ERR_INVALID_ARG)
  * o, lse outputs as in ks_evict_attn_fwd (lse required)
  * dtype  KS_BF16 with D = 128 (else KS_ERR_UNSUPPORTED); base > 1.
  * ws     workspace of at least ks_evict_attn_fwd_rope_workspace() bytes

@@ -806,6 +806,14 @@ extern "C" ks_status ks_evict_attn_fwd_rope(const void* q, const void* k, const 
   };
   KS_REQUIRE(!overlap(q, nq, q_rot, nq) && !overlap(k, nk, k_rot, nk),
              "%s: q_rot and k_rot must not alias q and k", name);
+  // the keys are rotated before the attention reads q, k and v, and q_rot
+  // and o are written by the same kernel: the three outputs must not touch
+  // the inputs or each other
+  KS_REQUIRE(!overlap(k_rot, nk, q, nq) && !overlap(k_rot, nk, v, nk) &&
+                 !overlap(q_rot, nq, k, nk) && !overlap(q_rot, nq, v, nk) &&
+                 !overlap(q_rot, nq, k_rot, nk) && !overlap(o, nq, q_rot, nq) &&
+                 !overlap(o, nq, k_rot, nk),
+             "%s: q_rot, k_rot and o must not overlap the inputs or each other", name);
   const size_t need = summary_bytes(B, N) + rope_table_bytes(B, N, D);
   if (!ws || ws_bytes < need)
     return ks_fail(KS_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);

@@ -236,7 +236,14 @@ def test_fused_rope_attention_argument_checks(lib):
     st, msg = fwd(q, k, FAKE, FAKE, FAKE, qr, k, FAKE, FAKE, B, N, H, H, D, ks.KS_BF16, 0.1,
                   10000.0, big, need_f, None)
     assert st == 1 and "alias" in msg                       # k_rot is k
-    st, _ = fwd(q, k, FAKE, FAKE, FAKE, qr, kr, FAKE, FAKE, B, N, H, H, D, ks.KS_BF16, 0.1,
+    v, o = ctypes.c_void_p(5 << 24), ctypes.c_void_p(6 << 24)
+    st, msg = fwd(q, k, v, FAKE, FAKE, qr, v, o, FAKE, B, N, H, H, D, ks.KS_BF16, 0.1,
+                  10000.0, big, need_f, None)
+    assert st == 1 and "overlap" in msg                     # k_rot is v
+    st, msg = fwd(q, k, v, FAKE, FAKE, qr, kr, qr, FAKE, B, N, H, H, D, ks.KS_BF16, 0.1,
+                  10000.0, big, need_f, None)
+    assert st == 1 and "overlap" in msg                     # o is q_rot
+    st, _ = fwd(q, k, v, FAKE, FAKE, qr, kr, o, FAKE, B, N, H, H, D, ks.KS_BF16, 0.1,
                 10000.0, big, need_f - 1, None)
     assert st == 4                                          # workspace short of the table
     st, msg = fwd(q, k, FAKE, FAKE, FAKE, qr, kr, FAKE, None, B, N, H, H, D, ks.KS_BF16, 0.1,
