@@ -145,7 +145,9 @@ def test_trace_past_one_live_window():
     in windows of 2,048 tiles (131,072 tokens), so query tiles past that
     point gather theirs from two windows (the pinned prompt and older recent
     turns in the first, the newest turns in the second).  Sampled rows there
-    and key blocks on both sides of the boundary against the oracle."""
+    and key blocks on both sides of the boundary against the oracle, through
+    the fused RoPE entry points (positions 0..N-1; gradients of the raw
+    projections)."""
     N, Hq, Hkv, D = 132096, 8, 2, 128
     G = Hq // Hkv
     tr = build_trace(np.random.default_rng(77), N, 512, 8192, "recent")
@@ -157,12 +159,15 @@ def test_trace_past_one_live_window():
     v = normal_tensor((1, N, Hkv, D), 7703, 0.5, bf, DEV)
     do = normal_tensor((1, N, Hq, D), 7704, 0.5, bf, DEV)
     eg = torch.from_numpy(e).to(DEV)
-    o, lse = ks.ks_evict_attn_fwd(q, k, v, eg)
-    dq, dk, dv = ks.ks_evict_attn_bwd(q, k, v, eg, o, lse, do)
+    pos = torch.arange(N, dtype=torch.int32, device=DEV)[None].contiguous()
+    o, lse, q_rot, k_rot = ks.ks_evict_attn_fwd_rope(q, k, v, eg, pos)
+    dq, dk, dv = ks.ks_evict_attn_bwd_rope(q_rot, k_rot, v, eg, pos, o, lse, do)
+    del q_rot, k_rot
     torch.cuda.synchronize()
     hkv = 1
     heads = slice(hkv * G, (hkv + 1) * G)
-    qh, kh, vh, doh = (f64(q[:, :, heads]), f64(k[:, :, hkv:hkv + 1]),
+    pn = np.arange(N)[None]
+    qh, kh, vh, doh = (O.rope(f64(q[:, :, heads]), pn), O.rope(f64(k[:, :, hkv:hkv + 1]), pn),
                        f64(v[:, :, hkv:hkv + 1]), f64(do[:, :, heads]))
     w = 2048 * 64
     rng = np.random.default_rng(78)
@@ -176,10 +181,11 @@ def test_trace_past_one_live_window():
         ro, rl = O.attn_fwd_rows(qh, kh, vh, e64, 0, hh, rows)
         gate(o[0, rows, hkv * G + hh], ro, "bf16", f"O rows h{hh}")
         gate(lse[0, hkv * G + hh, rows], rl, "bf16", f"LSE rows h{hh}")
-        rdq = O.attn_bwd_rows(qh, kh, vh, e64, doh, 0, hh, rows)
-        mdq = RM.dq_rows(qh, kh, vh, e64, doh, 0, hh, rows)
+        rdq = RM.unrotate_rows(O.attn_bwd_rows(qh, kh, vh, e64, doh, 0, hh, rows), rows)
+        mdq = RM.dq_rows(qh, kh, vh, e64, doh, 0, hh, rows, pos=rows)
         gate_rows_model(dq[0, rows, hkv * G + hh], rdq, mdq, f"dQ rows h{hh}")
     for keys in (np.arange(N - 64, N), np.arange(w - 32, w + 32)):
         rdk, rdv = O.attn_bwd_keys(qh, kh, vh, e64, doh, 0, 0, keys)
+        rdk = RM.unrotate_rows(rdk, keys)
         gate(dk[0, keys, hkv], rdk, "bf16grad", f"dK keys {keys[0]}..")
         gate(dv[0, keys, hkv], rdv, "bf16grad", f"dV keys {keys[0]}..")
