@@ -105,6 +105,48 @@ def test_compact_rounds_long_rows(B, MB, R, seed, with_pos):
         np.testing.assert_array_equal(po.cpu().numpy(), rp)
 
 
+@pytest.mark.parametrize("MB,seed", [(40001, 0), (65536, 1), (4103, 2)])
+def test_compact_rounds_runs_of_flags(MB, seed):
+    """Flags in runs, as eviction writes them (whole 64-flag windows of one
+    value, with run ends at any offset), with keep runs of 1, of other nonzero
+    bytes and of mixed nonzero bytes, on rows that start at every alignment
+    (odd row lengths), vs the oracle's event-by-event splice."""
+    rng = np.random.default_rng(900 + seed)
+    B, R = 7, 5
+    table = rng.integers(0, 2**31 - 1, size=(B, MB)).astype(np.int32)
+    pos = rng.integers(0, 2**31 - 1, size=(B, MB)).astype(np.int32)
+    nblk = rng.integers(MB // 2, MB + 1, size=B).astype(np.int32)
+    nblk[0] = MB
+    keeps = np.ones((R, B, MB), np.uint8)
+    for r in range(R):
+        for b in range(B):
+            row = keeps[r, b]
+            for _ in range(int(rng.integers(0, 6))):       # evicted runs
+                a = int(rng.integers(0, MB))
+                row[a:a + int(rng.integers(1, 3000))] = 0
+            kind = (r + b) % 4
+            if kind == 1:                                  # keep written as 0xff
+                row[row == 1] = 255
+            elif kind == 2:                                # a run of another value
+                a = int(rng.integers(0, MB))
+                seg = row[a:a + int(rng.integers(1, 5000))]
+                seg[seg == 1] = int(rng.integers(2, 256))
+            elif kind == 3:                                # single odd bytes among ones
+                idx = rng.integers(0, MB, size=8)
+                row[idx] = np.where(row[idx] == 1, 7, row[idx])
+    keeps[:, 6] = 0                                        # a row evicted whole
+    rt, rn, rp = _oracle_rounds(table, nblk, keeps, pos)
+    out = torch.full((B, MB), 7, dtype=torch.int32, device=DEV)
+    po = torch.full((B, MB), 7, dtype=torch.int32, device=DEV)
+    n_out = torch.empty(B, dtype=torch.int32, device=DEV)
+    ks.ks_compact_block_table_rounds(_gpu(table), _gpu(nblk), _gpu(keeps), out, n_out,
+                                     _gpu(pos), po)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), rt)
+    np.testing.assert_array_equal(n_out.cpu().numpy(), rn)
+    np.testing.assert_array_equal(po.cpu().numpy(), rp)
+
+
 def test_compact_rounds_token_batch():
     db = build_decode_batch(workload_rng(PAGED_DECODE), 64, block=1)
     out, n, _ = ks.ks_compact_block_table_rounds(_gpu(db.table0), _gpu(db.nblk0),
