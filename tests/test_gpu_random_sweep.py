@@ -69,6 +69,43 @@ def test_attention_random_shapes(seed):
 
 
 @pytest.mark.parametrize("seed", range(8))
+def test_fused_rope_random_shapes(seed):
+    """The training step's entry points (RoPE fused into the forward and the
+    backward) on random shapes, records and logical positions with gaps,
+    against the oracle's outputs and its gradients of the unrotated
+    projections (the gradients of the rotated operands rotated back)."""
+    rng = np.random.default_rng(9300 + seed)
+    B = int(rng.integers(1, 4))
+    N = int(rng.integers(1, 300)) if seed % 2 else int(rng.integers(300, 2500))
+    Hkv = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    Hq, D = Hkv * G, 128
+    e = _record(rng, B, N)
+    steps = 1 + (rng.random((B, N)) < 0.1) * rng.integers(1, 400, (B, N))
+    pos = (np.cumsum(steps, axis=1) - 1 + rng.integers(0, 5000, (B, 1))).astype(np.int32)
+    s0 = 9300 + 10 * seed
+    q = normal_tensor((B, N, Hq, D), s0, 0.5, bf)
+    k = normal_tensor((B, N, Hkv, D), s0 + 1, 0.5, bf)
+    v = normal_tensor((B, N, Hkv, D), s0 + 2, 0.5, bf)
+    do = normal_tensor((B, N, Hq, D), s0 + 3, 0.5, bf)
+    eg = torch.from_numpy(e.astype(np.int32)).to(DEV)
+    pg = torch.from_numpy(pos).to(DEV)
+    qg, kg, vg, dog = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse, q_rot, k_rot = ks.ks_evict_attn_fwd_rope(qg, kg, vg, eg, pg)
+    dq, dk, dv = ks.ks_evict_attn_bwd_rope(q_rot, k_rot, vg, eg, pg, o, lse, dog)
+    torch.cuda.synchronize()
+    tag = f"B={B} N={N} Hq={Hq} Hkv={Hkv}"
+    qr, kr = O.rope(f64(q), pos), O.rope(f64(k), pos)
+    ro, rl = O.attn_fwd(qr, kr, f64(v), e)
+    gate(o, ro, "bf16", f"O {tag}")
+    gate(lse, rl, "bf16", f"LSE {tag}")
+    rdq, rdk, rdv = O.attn_bwd(qr, kr, f64(v), e, f64(do))
+    gate(dq, O.rope(rdq, pos, inverse=True), "bf16grad", f"dQ (unrotated) {tag}")
+    gate(dk, O.rope(rdk, pos, inverse=True), "bf16grad", f"dK (unrotated) {tag}")
+    gate(dv, rdv, "bf16grad", f"dV {tag}")
+
+
+@pytest.mark.parametrize("seed", range(8))
 def test_decode_random_shapes(seed):
     rng = np.random.default_rng(9500 + seed)
     block = int(rng.choice([16, 1]))
