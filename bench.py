@@ -19,6 +19,8 @@ one pool slot per token (token tables, token-run compaction), and
 3-layer model built on the path, and `reprefill_counterfactual` times,
 outside the step, the
 attention that re-prefill compaction would run on the same rollouts.
+`long_mixed_64k` times the fwd+bwd of 8 x 64k traces under three compaction
+strategies and their continuation by 256 decode steps with a forced event.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same workload
 on the host cores.
 """
@@ -631,7 +633,8 @@ def long_mixed_64k(ks, torch, stream, reps=5):
     compacted by sliding window, prompt+recent and summary in turn, 64 q /
     8 kv heads, D = 128.  Median over reps of each pass, timed with HIP
     events on the library's stream; useful TFLOP/s with the step's
-    convention (RoPE fused into the timed forward and backward)."""
+    convention (RoPE fused into the timed forward and backward).  Then the
+    traces continued by 256 decode steps (long_mixed_decode)."""
     from workloads import LONG_MIXED_64K, config_trace_batch, normal_tensor, stacked_e
 
     cfg = LONG_MIXED_64K
@@ -691,9 +694,98 @@ def long_mixed_64k(ks, torch, stream, reps=5):
         "bwd_tflops_useful": round(useful_b / (mb * 1e-3) / 1e12, 2),
         "executed_over_useful": round((ex_f + ex_q + ex_kv) / (useful_f + useful_b), 4),
     }
-    del q, k, v, do, o, dq, dk, dv, wsf, wsb, q_rot, k_rot
+    del q, do, o, dq, dk, dv, wsf, wsb, q_rot
+    torch.cuda.empty_cache()
+    # the traces continued by 256 decoded tokens with a forced event after 128
+    out["decode_256"] = long_mixed_decode(ks, torch, stream, traces, cfg, k_rot, v)
+    del k, v, k_rot
     torch.cuda.empty_cache()
     return out
+
+
+def long_mixed_decode(ks, torch, stream, traces, cfg, k_rot, v, ndec=256, event_after=128,
+                      reps=3):
+    """The long mixed traces continued by decoding, as the decode step runs:
+    each trace's live set (keys as the training pass rotated them) in a
+    16-token-block pool with ndec / 16 fresh blocks, then ndec steps over all
+    traces of ks_append_kv (the new key rotated at position N + s) and
+    ks_paged_decode_rope (the query rotated in the kernel), with the forced
+    compaction event after event_after tokens (ks_compact_block_table).  The
+    ndec steps run back to back on the stream between two HIP events (median
+    of reps); tokens, lengths and positions are resident before the timed
+    region, and the tables are reset between reps outside it."""
+    from workloads import BLOCK, continuation_layout, normal_tensor
+
+    B, N, Hq, Hkv, D = cfg.batch, cfg.N, cfg.Hq, cfg.Hkv, cfg.D
+    dev, bf = "cuda", torch.bfloat16
+    lay = continuation_layout(traces, N, ndec, event_after, np.random.default_rng(5005))
+    NB, MB = lay.num_pool_blocks, lay.table0.shape[1]
+    kp = torch.zeros((NB, Hkv, BLOCK, D), dtype=bf, device=dev)
+    vp = torch.zeros_like(kp)
+    for b in range(B):
+        L = int(lay.live_len[b])
+        blk = torch.from_numpy(np.repeat(lay.table0[b, :L // BLOCK], BLOCK).astype(np.int64)).to(dev)
+        slot = torch.arange(L, device=dev) % BLOCK
+        tok = torch.from_numpy(lay.live_tok[b].astype(np.int64)).to(dev)
+        kp[blk, :, slot] = k_rot[b, tok]
+        vp[blk, :, slot] = v[b, tok]
+    qn = normal_tensor((ndec, B, Hq, D), 7001, 0.5, bf, dev)
+    kn = normal_tensor((ndec, B, Hkv, D), 7002, 0.5, bf, dev)
+    vn = normal_tensor((ndec, B, Hkv, D), 7003, 0.5, bf, dev)
+    lens = np.empty((ndec, B), np.int64)
+    length = lay.live_len.astype(np.int64)
+    for s in range(ndec):
+        if s == event_after:
+            length = length - lay.ev_tokens
+        length = length + 1
+        lens[s] = length
+    seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    posn = torch.arange(N, N + ndec, dtype=torch.int32, device=dev)[:, None].repeat(1, B)
+    table0 = torch.from_numpy(lay.table0).to(dev)
+    nblk0 = torch.from_numpy(lay.nblk0).to(dev)
+    keep = torch.from_numpy(lay.keep).to(dev)
+    tab, nblk = torch.empty_like(table0), torch.empty_like(nblk0)
+    tab2, nblk2 = torch.empty_like(table0), torch.empty_like(nblk0)
+    out = torch.empty((B, Hq, D), dtype=bf, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(ks.ks_paged_decode_workspace(B, Hq, D, MB * BLOCK), dtype=torch.uint8,
+                     device=dev)
+
+    def steps():
+        t = tab
+        for s in range(ndec):
+            if s == event_after:
+                ks.ks_compact_block_table(tab, nblk, keep, tab2, nblk2, stream=stream)
+                t = tab2
+            ks.ks_append_kv(kn[s], vn[s], posn[s], t, seq[s], kp, vp, stream=stream)
+            ks.ks_paged_decode_rope(qn[s], posn[s], kp, vp, t, seq[s], out=out, lse=lse, ws=ws,
+                                    stream=stream)
+
+    times = []
+    for r in range(reps + 1):                    # the first pass is a warm-up
+        tab.copy_(table0)
+        nblk.copy_(nblk0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        steps()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r:
+            times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    # per step as for the 64-sequence decode: K and V of every live token,
+    # q, the new k and v (read and written), out, lse, table entries, lengths
+    per_step = [int((Ls * Hkv * D * 2 * 2).sum()) + B * Hq * D * 2 + 2 * 2 * B * Hkv * D * 2 +
+                B * Hq * D * 2 + B * Hq * 4 + int(((Ls + 15) // 16).sum()) * 4 + B * 4
+                for Ls in lens]
+    dec_bytes = sum(per_step)
+    del kp, vp, ws
+    return {"steps": ndec, "event_after": event_after,
+            "evicted_tokens_per_trace": [int(x) for x in lay.ev_tokens],
+            "ms_total": round(ms, 3), "us_per_step": round(ms * 1e3 / ndec, 1),
+            "hbm_gbs": round(dec_bytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(dec_bytes / (ms * 1e-3) / 8e12, 4)}
 
 
 def mfma_rate(ks, torch, stream, workgroups=2048, iters=2500):

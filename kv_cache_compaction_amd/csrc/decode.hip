@@ -7,7 +7,8 @@
 // reached through the table.
 //
 // Kernel 1 (split): one 64-lane wave per (sequence, group of HPW query heads
-// of one kv head, split of kSplit blocks).  The split's block ids are read
+// of one kv head, split of 48 blocks, or 16 when the grid would be small:
+// split_groups).  The split's block ids are read
 // once, one per lane; each block's id is then taken with readlane.  Lane
 // (t, g) = (lane % 16, lane / 16) owns token slot t of every block and the 32
 // head-dim entries
@@ -29,8 +30,8 @@
 // Single-token blocks (BS = 1, the SGLang setup: explainer, paragraph on
 // padding completions to whole blocks): the table lists one pool slot per
 // token and the pool is [slots, Hkv, D].  The same kernels run over groups
-// of 16 consecutive table entries; the split's 768 slot ids are staged in LDS
-// once and lane (t, g) reads the id of its own token slot t of each group, so
+// of 16 consecutive table entries; the split's slot ids (up to 768) are
+// staged in LDS once and lane (t, g) reads the id of its own token slot t of each group, so
 // every load instruction still covers 64 contiguous bytes of 16 token rows
 // (now 16 separate rows of the pool).
 //
@@ -48,6 +49,12 @@ namespace {
 constexpr int D = 128;
 constexpr int kSplit = 48;     // 16-token groups per split (block ids fit one wave)
 static_assert(kSplit <= 64, "one block id per lane");
+// Shorter splits when 48-group splits would give a small grid (fewer than
+// kFewWaves waves, about two rounds of the GPU's wave slots): a step then
+// spends most of its time in the last waves' full splits, while in large
+// grids every extra split is extra start-up, merge and partial traffic.
+constexpr int kSplitSmall = 16;
+constexpr long long kFewWaves = 4096;
 constexpr float kTau = 8.0f;   // lazy-rescale slack, log2 units
 
 template <int CTRL>
@@ -83,7 +90,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kpool,
     const bf16_t* __restrict__ vpool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int Hq, int Hkv, int MB, int NB, int nsplit_max,
+    float* __restrict__ part_ml, int Hq, int Hkv, int MB, int NB, int nsplit_max, int sg,
     float sl2, const int32_t* __restrict__ qpos, double log2_base) {
   static_assert(BS == 16 || BS == 1, "block size");
   const int hw = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
@@ -94,9 +101,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   // row is ever read
   const int L = min(max(seq_lens[b], 0), BS * MB);
   const int nblk = (L + 15) >> 4;     // 16-token groups
-  const int blk0 = split * kSplit;
+  const int blk0 = split * sg;
   if (blk0 >= nblk) return;
-  const int blk1 = min(nblk, blk0 + kSplit);
+  const int blk1 = min(nblk, blk0 + sg);
   const int lane = threadIdx.x;
   const int t = lane & 15, g = lane >> 4;
 
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
       const int tok = blk0 * 16 + i * 64 + lane;
-      v[i] = tok < L ? trow[tok] : 0;
+      v[i] = tok < min(L, blk1 * 16) ? trow[tok] : 0;
     }
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) sid[i * 64 + lane] = v[i];
@@ -266,10 +273,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 __global__ __launch_bounds__(D) void decode_reduce_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, bf16_t* __restrict__ out, float* __restrict__ lse,
-    int Hq, int cap, int nsplit_max) {
+    int Hq, int cap, int nsplit_max, int sg) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int L = min(max(seq_lens[b], 0), cap);
-  const int ns = (((L + 15) >> 4) + kSplit - 1) / kSplit;
+  const int ns = (((L + 15) >> 4) + sg - 1) / sg;
   const size_t slot0 = (static_cast<size_t>(b) * Hq + h) * nsplit_max;
   // splits in groups of 8 whose loads are all issued before their use (a
   // plain loop waits for each load in turn); the sums run in split order
@@ -359,12 +366,23 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
 }
 
-// splits for a table row of `groups` 16-token groups
-inline int nsplit_for(int groups) { return (groups + kSplit - 1) / kSplit; }
+// 16-token groups per split for B sequences of Hq query heads over table
+// rows of `groups` groups: decided from the sizes alone (the workspace query
+// and the launch see the same ones), with the waves counted at four query
+// heads per wave
+inline int split_groups(int B, int Hq, int groups) {
+  const long long waves = static_cast<long long>(B) * ((Hq + 3) / 4) *
+                          ((groups + kSplit - 1) / kSplit);
+  return waves < kFewWaves ? kSplitSmall : kSplit;
+}
+
+// splits for a table row of `groups` 16-token groups, `sg` groups per split
+inline int nsplit_for(int groups, int sg) { return (groups + sg - 1) / sg; }
 
 inline size_t decode_workspace(int B, int Hq, int Dh, int groups) {
   if (B <= 0 || Hq <= 0 || Dh <= 0 || groups <= 0) return 0;
-  const size_t slots = static_cast<size_t>(B) * Hq * nsplit_for(groups);
+  const size_t slots =
+      static_cast<size_t>(B) * Hq * nsplit_for(groups, split_groups(B, Hq, groups));
   return slots * (static_cast<size_t>(Dh) + 2) * sizeof(float) + 256;
 }
 
@@ -399,7 +417,8 @@ ks_status decode_impl(const char* name, const void* q, const void* k_pool, const
   const size_t need = decode_workspace(B, Hq, Dh, groups);
   if (!ws || ws_bytes < need)
     return ks_fail(KS_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
-  const int nsplit = nsplit_for(groups);
+  const int sg = split_groups(B, Hq, groups);
+  const int nsplit = nsplit_for(groups, sg);
   KS_REQUIRE(nsplit < 65536 && B < 65536, "%s: grid too large", name);
   float* part_ml = static_cast<float*>(ws);
   const size_t slots = static_cast<size_t>(B) * Hq * nsplit;
@@ -415,20 +434,20 @@ ks_status decode_impl(const char* name, const void* q, const void* k_pool, const
   const bf16_t* vp = static_cast<const bf16_t*>(v_pool);
   if (hpw == 4)
     hipLaunchKernelGGL((decode_split_kernel<4, BS>), grid, dim3(64), 0, s, qq, kp, vp, table,
-                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2,
+                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sg, sl2,
                        qpos, log2_base);
   else if (hpw == 2)
     hipLaunchKernelGGL((decode_split_kernel<2, BS>), grid, dim3(64), 0, s, qq, kp, vp, table,
-                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2,
+                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sg, sl2,
                        qpos, log2_base);
   else
     hipLaunchKernelGGL((decode_split_kernel<1, BS>), grid, dim3(64), 0, s, qq, kp, vp, table,
-                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sl2,
+                       seq_lens, part_o, part_ml, Hq, Hkv, max_entries, num_pool, nsplit, sg, sl2,
                        qpos, log2_base);
   ks_status st = ks_check_launch(name);
   if (st != KS_OK) return st;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(Hq, B), dim3(D), 0, s, part_o, part_ml, seq_lens,
-                     static_cast<bf16_t*>(out), lse, Hq, max_entries * BS, nsplit);
+                     static_cast<bf16_t*>(out), lse, Hq, max_entries * BS, nsplit, sg);
   return ks_check_launch(name);
 }
 

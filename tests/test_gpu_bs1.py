@@ -186,8 +186,9 @@ def _direct_bs1(B, Hq, Hkv, lens, seed, extra=7):
 @pytest.mark.parametrize("Hq,Hkv,seed", [(32, 8, 1), (8, 4, 2), (4, 4, 3), (12, 4, 4),
                                          (12, 2, 5)])
 def test_decode_bs1_ragged_lengths(Hq, Hkv, seed):
-    # 768 = one split of 48 groups of 16 tokens
-    lens = np.array([0, 1, 15, 16, 17, 767, 768, 769, 1537, 3001], np.int32)
+    # 256 and 768: one split of 16 or of 48 groups of 16 tokens (this small
+    # grid takes 16-group splits)
+    lens = np.array([0, 1, 15, 16, 17, 255, 256, 257, 767, 768, 769, 1537, 3001], np.int32)
     B = len(lens)
     q, kp, vp, table = _direct_bs1(B, Hq, Hkv, lens, 100 + seed)
     out, lse = ks.ks_paged_decode_bs1(q, kp, vp, _gpu(table), _gpu(lens))
@@ -250,7 +251,7 @@ def test_decode_bs1_invalid_slot_in_a_later_split():
     lens = np.array([40, 40, 1600], np.int32)
     q, kp, vp, table = _direct_bs1(3, 32, 8, lens, 700)
     table[1, 33] = kp.shape[0] + 5          # out of range
-    table[2, 1500] = -3                     # in the second 768-token split
+    table[2, 1500] = -3                     # past the first split (256 or 768 tokens)
     out, _ = ks.ks_paged_decode_bs1(q, kp, vp, _gpu(table), _gpu(lens))
     torch.cuda.synchronize()
     assert torch.isfinite(out[0].float()).all()

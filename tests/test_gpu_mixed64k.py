@@ -12,8 +12,8 @@ import kv_cache_compaction_amd as ks
 import oracle as O
 import rounding_model as RM
 from parity_util import announce, f64, gate, gate_rows_model, oracle_bwd_keys
-from workloads import (BLOCK, KS_NEVER, LONG_MIXED_64K, config_trace_batch, evict_units,
-                       normal_tensor, stacked_e)
+from workloads import (BLOCK, KS_NEVER, LONG_MIXED_64K, config_trace_batch,
+                       continuation_layout, normal_tensor, stacked_e)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -144,48 +144,19 @@ def test_mixed64k_decode_with_forced_compaction(run):
     B, N, Hq, Hkv, D = CFG.batch, CFG.N, CFG.Hq, CFG.Hkv, CFG.D
     G = Hq // Hkv
     bf = torch.bfloat16
-    rng = np.random.default_rng(5005)
-    # --- pool and tables: live tokens of the trace, then NDEC/16 fresh blocks
-    live_tok = [np.concatenate([np.arange(x, y) for (x, y) in tr.live_units]) for tr in traces]
-    L0 = np.array([len(t) for t in live_tok])
-    assert np.all(L0 % BLOCK == 0)
-    nfresh = NDEC // BLOCK
-    nblk0 = L0 // BLOCK + nfresh
-    MB = int(nblk0.max())
-    NB = int(nblk0.sum())
-    perm = rng.permutation(NB).astype(np.int32)
-    table0 = np.full((B, MB), -1, np.int32)
-    logical = []                                  # first token of each listed block
-    off = 0
-    for b in range(B):
-        n = int(nblk0[b])
-        table0[b, :n] = perm[off:off + n]
-        off += n
-        logical.append(np.concatenate([live_tok[b][::BLOCK], N + BLOCK * np.arange(nfresh)]))
+    # --- pool and tables: live tokens of the trace, then NDEC/16 fresh blocks;
+    # the forced event after token EVENT_AFTER
+    lay = continuation_layout(traces, N, NDEC, EVENT_AFTER, np.random.default_rng(5005))
+    table0, nblk0, L0, NB = lay.table0, lay.nblk0, lay.live_len, lay.num_pool_blocks
     kp = torch.full((NB, Hkv, BLOCK, D), float("nan"), dtype=bf, device=DEV)
     vp = torch.full((NB, Hkv, BLOCK, D), float("nan"), dtype=bf, device=DEV)
     for b in range(B):
         blk = torch.from_numpy(np.repeat(table0[b, :L0[b] // BLOCK], BLOCK).astype(np.int64)).to(DEV)
         slot = torch.arange(L0[b], device=DEV) % BLOCK
-        tok = torch.from_numpy(live_tok[b].astype(np.int64)).to(DEV)
+        tok = torch.from_numpy(lay.live_tok[b].astype(np.int64)).to(DEV)
         kp[blk, :, slot] = run["k_rot"][b, tok]
         vp[blk, :, slot] = run["v"][b, tok]
-    # --- the forced event after token EVENT_AFTER: evicted spans per trace
-    t_ev = N + EVENT_AFTER
-    ev_spans = []
-    for tr in traces:
-        units = list(tr.live_units) + [(N, t_ev)]
-        P = tr.P
-        _, out = evict_units(units, t_ev, tr.strategy, tr.budget, P, tr.overlap, tr.summary)
-        ev_spans.append(out)
-    keep = np.zeros((B, MB), np.uint8)
-    ev_tokens = np.zeros(B, np.int64)
-    for b in range(B):
-        gone = np.zeros(N + NDEC, bool)
-        for (x, y) in ev_spans[b]:
-            gone[x:y] = True
-            ev_tokens[b] += y - x
-        keep[b, :nblk0[b]] = ~gone[logical[b]]
+    keep, ev_tokens, ev_spans, t_ev = lay.keep, lay.ev_tokens, lay.ev_spans, lay.t_ev
     # --- decode inputs (raw), seeded
     qn = normal_tensor((NDEC, B, Hq, D), 7001, 0.5, bf, DEV)
     kn = normal_tensor((NDEC, B, Hkv, D), 7002, 0.5, bf, DEV)

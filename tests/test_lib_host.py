@@ -265,3 +265,22 @@ def test_fused_rope_attention_argument_checks(lib):
     st, _ = bwd(None, None, None, None, None, None, None, None, None, None, None, B, 0, H, H, D,
                 ks.KS_BF16, 0.1, 10000.0, None, 0, None)
     assert st == 0                                          # N == 0 is a no-op
+
+
+def test_decode_split_length_follows_the_grid(lib):
+    """The decode's split length is chosen from the sizes alone: 48-group
+    splits, or 16-group splits when 48-group splits would give fewer than
+    4096 waves (four query heads per wave).  The workspace query shows the
+    choice: (D + 2) floats per (sequence, head, split), plus 256 bytes."""
+    def slots(B, Hq, groups, sg):
+        return B * Hq * ((groups + sg - 1) // sg)
+    # 8 sequences, 64 heads, 1036-group rows: 8 * 16 * 22 = 2816 waves -> 16
+    assert lib.ks_paged_decode_workspace(8, 64, 128, 1036) == slots(8, 64, 1036, 16) * 130 * 4 + 256
+    # 64 sequences, 32 heads, 4097-group rows: 64 * 8 * 86 waves -> 48
+    assert lib.ks_paged_decode_workspace(64, 32, 128, 4097) == slots(64, 32, 4097, 48) * 130 * 4 + 256
+    # just below and at the threshold (one head per wave counted as 4 heads / 4)
+    assert lib.ks_paged_decode_workspace(1, 4, 128, 48 * 4095) == slots(1, 4, 48 * 4095, 16) * 130 * 4 + 256
+    assert lib.ks_paged_decode_workspace(1, 4, 128, 48 * 4096) == slots(1, 4, 48 * 4096, 48) * 130 * 4 + 256
+    # token tables count 16 tokens per group
+    assert lib.ks_paged_decode_bs1_workspace(8, 64, 128, 16 * 1036) == \
+        lib.ks_paged_decode_workspace(8, 64, 128, 1036)

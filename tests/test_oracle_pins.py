@@ -528,6 +528,37 @@ def test_decode_batch_structure():
             assert x0 >= 1 and x1 <= db.nblk0[b] - 2
 
 
+def test_continuation_layout_structure():
+    """The long mixed traces continued by 256 decoded tokens: every live
+    token sits in a listed block in trace order, block ids are unique, the
+    fresh blocks follow at N, N + 16, ..., and the forced event's flags drop
+    exactly the listed blocks its spans cover (whole blocks only)."""
+    from workloads import LONG_MIXED_64K, continuation_layout
+    traces, _ = config_trace_batch(LONG_MIXED_64K)
+    N = LONG_MIXED_64K.N
+    lay = continuation_layout(traces, N, 256, 128, np.random.default_rng(5005))
+    B = len(traces)
+    ids = np.concatenate([lay.table0[b, :lay.nblk0[b]] for b in range(B)])
+    assert len(np.unique(ids)) == len(ids) == lay.num_pool_blocks
+    assert np.all(lay.table0[np.arange(lay.table0.shape[1])[None] >= lay.nblk0[:, None]] == -1)
+    assert lay.t_ev == N + 128
+    for b, tr in enumerate(traces):
+        live = lay.live_tok[b]
+        assert len(live) == lay.live_len[b] == sum(y - x for x, y in tr.live_units)
+        assert np.all(np.diff(live) > 0) and live.max() < N
+        lg = lay.logical[b]
+        assert len(lg) == lay.nblk0[b] and np.all(lg % 16 == 0)
+        assert np.array_equal(lg[-16:], N + 16 * np.arange(16))
+        assert np.array_equal(live.reshape(-1, 16), lg[:-16, None] + np.arange(16))
+        gone = np.zeros(N + 256, bool)
+        for x, y in lay.ev_spans[b]:
+            assert x % 16 == 0 and y % 16 == 0 and y <= lay.t_ev
+            gone[x:y] = True
+        assert lay.ev_tokens[b] == gone.sum() > 0
+        assert np.array_equal(lay.keep[b, :lay.nblk0[b]], ~gone[lg])
+        assert not lay.keep[b, lay.nblk0[b]:].any()
+
+
 # ---------------------------------------------------------------------------
 # Single-token blocks (token-granular traces, tables and decode)
 # ---------------------------------------------------------------------------

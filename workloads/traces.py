@@ -334,6 +334,70 @@ def build_decode_batch(rng: np.random.Generator, n_seqs: int,
                        num_pool_blocks=NB, block=bs)
 
 
+@dataclass
+class Continuation:
+    """Paged layout of training traces continued by decoding (see
+    ``continuation_layout``)."""
+    table0: np.ndarray      # [B, MB] physical block ids, -1 past nblk0
+    nblk0: np.ndarray       # [B] listed blocks: the live set, then the fresh blocks
+    live_len: np.ndarray    # [B] live tokens at the end of each trace
+    live_tok: list          # per trace: trace indices of its live tokens, in order
+    logical: list           # per trace: first trace index of each listed block
+    num_pool_blocks: int
+    keep: np.ndarray        # [B, MB] uint8 flags of the forced event over the listed blocks
+    ev_spans: list          # per trace: the spans the forced event evicts
+    ev_tokens: np.ndarray   # [B] tokens the forced event evicts
+    t_ev: int               # trace index of the forced event
+
+
+def continuation_layout(traces, N: int, ndec: int, event_after: int,
+                        rng: np.random.Generator, block: int = BLOCK) -> Continuation:
+    """Training traces of length ``N`` continued by ``ndec`` decoded tokens.
+
+    Each trace's live set at its end fills whole ``block``-token blocks of one
+    shared pool (physical ids a seeded permutation), followed by
+    ``ndec / block`` fresh blocks for the decoded tokens at trace indices
+    ``N, N + 1, ...``.  After ``event_after`` new tokens a forced compaction
+    event at ``t_ev = N + event_after`` applies the trace's own strategy to
+    its live spans plus the decoded span; ``keep`` holds that event's flags
+    over the listed blocks.
+    """
+    B = len(traces)
+    live_tok = [np.concatenate([np.arange(x, y) for (x, y) in tr.live_units]) for tr in traces]
+    L0 = np.array([len(t) for t in live_tok])
+    assert np.all(L0 % block == 0) and ndec % block == 0
+    nfresh = ndec // block
+    nblk0 = (L0 // block + nfresh).astype(np.int32)
+    MB = int(nblk0.max())
+    NB = int(nblk0.sum())
+    perm = rng.permutation(NB).astype(np.int32)
+    table0 = np.full((B, MB), -1, np.int32)
+    logical = []
+    off = 0
+    for b in range(B):
+        n = int(nblk0[b])
+        table0[b, :n] = perm[off:off + n]
+        off += n
+        logical.append(np.concatenate([live_tok[b][::block], N + block * np.arange(nfresh)]))
+    t_ev = N + event_after
+    ev_spans = []
+    for tr in traces:
+        units = list(tr.live_units) + [(N, t_ev)]
+        _, out = evict_units(units, t_ev, tr.strategy, tr.budget, tr.P, tr.overlap, tr.summary)
+        ev_spans.append(out)
+    keep = np.zeros((B, MB), np.uint8)
+    ev_tokens = np.zeros(B, np.int64)
+    for b in range(B):
+        gone = np.zeros(N + ndec, bool)
+        for (x, y) in ev_spans[b]:
+            gone[x:y] = True
+            ev_tokens[b] += y - x
+        keep[b, :nblk0[b]] = ~gone[logical[b]]
+    return Continuation(table0=table0, nblk0=nblk0, live_len=L0, live_tok=live_tok,
+                        logical=logical, num_pool_blocks=NB, keep=keep, ev_spans=ev_spans,
+                        ev_tokens=ev_tokens, t_ev=t_ev)
+
+
 def normal_tensor(shape, seed: int, scale: float = 1.0, dtype=None,
                   device: str = "cpu"):
     """N(0,1)*scale tensor, drawn in fp32 and rounded (RNE) to ``dtype`` once.
