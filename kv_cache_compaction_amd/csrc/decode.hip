@@ -278,9 +278,9 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   const int L = min(max(seq_lens[b], 0), cap);
   const int ns = (((L + 15) >> 4) + sg - 1) / sg;
   const size_t slot0 = (static_cast<size_t>(b) * Hq + h) * nsplit_max;
-  // splits in groups of 8 whose loads are all issued before their use (a
+  // splits in groups of 16 whose loads are all issued before their use (a
   // plain loop waits for each load in turn); the sums run in split order
-  constexpr int U = 8;
+  constexpr int U = 16;
   float M = -INFINITY;
   for (int s0 = 0; s0 < ns; s0 += U) {
     float m[U];
