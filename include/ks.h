@@ -387,10 +387,13 @@ ks_status ks_paged_decode_rope(const void* q, const int32_t* pos,
  * bytes (96 MiB) per GPU, kept until the process ends.  The call itself
  * allocates nothing (no hipMalloc, hipFree or allocating library routine).
  *
- * Limit   B * Hq * ceil(max_blocks / 48) split slots of (D + 2) floats must
- *         fit the array (e.g. 64 sequences x 32 query heads over tables of
- *         4,096 blocks); larger calls return KS_ERR_WORKSPACE before any
- *         launch -- use ks_paged_decode with a workspace for those.
+ * Limit   the call's split partials, ks_paged_decode_workspace(B, Hq, D,
+ *         max_blocks) bytes (B * Hq * ceil(max_blocks / S) split slots of
+ *         (D + 2) floats, S = 48 groups per split, or 16 when 48-group
+ *         splits would make fewer than 4096 waves), must fit the array (e.g.
+ *         64 sequences x 32 query heads over tables of 4,096 blocks); larger
+ *         calls return KS_ERR_WORKSPACE before any launch -- use
+ *         ks_paged_decode with a workspace for those.
  * Sharing Every call on one GPU uses that GPU's single array, which keeps the
  *         last call's contents (each call writes every entry it reads).
  *         Calls that overlap in time on one GPU -- on different streams or
