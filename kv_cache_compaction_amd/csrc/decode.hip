@@ -35,11 +35,13 @@
 // every load instruction still covers 64 contiguous bytes of 16 token rows
 // (now 16 separate rows of the pool).
 //
-// Memory: K and V of every live token are read exactly once per step; the
+// Memory: K and V of every live token are read from HBM once per step; the
 // split partials add 4(D+2) bytes per (sequence, head, split).  The grid runs
 // head groups fastest, so the Hkv waves reading the slices of one pool block
 // (Hkv x 16 x D contiguous elements of K, and of V) run side by side, which
-// keeps the DRAM accesses of concurrent waves on the same rows.
+// keeps the DRAM accesses of concurrent waves on the same rows.  When a kv
+// head has more query heads than one wave takes, its waves are placed on
+// one XCD, whose L2 then serves the second read of its slices.
 #include <mutex>
 
 #include "ks_common.h"
@@ -93,8 +95,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     float* __restrict__ part_ml, int Hq, int Hkv, int MB, int NB, int nsplit_max, int sg,
     float sl2, const int32_t* __restrict__ qpos, double log2_base) {
   static_assert(BS == 16 || BS == 1, "block size");
-  const int hw = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
+  // the G / HPW waves of one kv head read the same K/V slices: x = kv + Hkv *
+  // sub puts them Hkv workgroups apart, and consecutive workgroups go to the
+  // XCDs in turn, so with Hkv a multiple of 8 they share one XCD's L2
+  const int hw = (blockIdx.x % Hkv) * (G / HPW) + blockIdx.x / Hkv;
+  const int split = blockIdx.y, b = blockIdx.z;
   const int hq0 = hw * HPW;
   const int hkv = hq0 / G;
   // lengths beyond the table's capacity are clamped: nothing past a table
